@@ -1,0 +1,247 @@
+"""CPU float64 oracle: attention written out from its definition.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring): never imported by the
+product path.
+
+Sources (the pages this follows; cited by page title and section):
+
+* FlashAttention: Part 2, section 2.1 "PyTorch Scaled-Dot-Product Attention
+  Today": the function is softmax(Q K^T / sqrt(d)) V.
+* FlashAttention: Part 2, section 3.2 and section 1.6: dense FlashAttention
+  evaluates that function for every required query/key pair, no pair
+  skipped, so the tiled method is exact up to rounding order and the oracle
+  is simply the definition.
+* FlashAttention: Part 2, section 1.3: one row-wise log-sum-exp per query row
+  is the per-row statistic kept next to the output.
+* pyshine.com FlashAttention code tour, "Why You Need This": grouped-query
+  attention lets K and V carry fewer heads than Q when the counts divide
+  evenly; decode with query length one splits the cache over thread blocks
+  and combines the partial results.
+* FlashAttention: Part 2, section 4.1: decode is one query row against the
+  whole key/value cache.
+* FlashAttention: Part 2, section 6.2 "FlashAttention Summary": the online
+  softmax state (m, l, a) and the rescale factor alpha = e^(m - m').
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes of the repository):
+
+* LSE is the natural log of the sum of e^(s) over the visible keys of the
+  *scaled* scores s = scale * <q, k>.
+* Causal is top-left aligned: key j is visible to query i iff j <= i.
+* Grouped heads are contiguous: query head hq reads key/value head
+  hq // (Hq // Hkv).
+* A row with no visible key has O = 0 and LSE = -inf.
+* Layout is (batch, sequence, heads, head_dim) for q, k, v and o; LSE is
+  (batch, heads, queries).
+
+Everything is float64. Inputs of any real dtype are converted with
+``numpy.asarray(..., dtype=float64)``, which is exact for bf16/fp32 values.
+"""
+
+import numpy as np
+
+__all__ = [
+    "kv_head_of",
+    "visible_mask",
+    "scores",
+    "softmax_rows",
+    "attention",
+    "attention_rows",
+    "decode",
+    "merge_partials",
+    "online_softmax_attention",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def kv_head_of(hq, Hq, Hkv):
+    """Key/value head read by query head ``hq`` (contiguous groups of Hq/Hkv).
+
+    pyshine.com FlashAttention code tour, "Why You Need This": K and V may
+    carry fewer heads than Q when the counts divide evenly. The grouping
+    order is not stated; contiguous groups are the reading taken here.
+    """
+    if Hkv <= 0 or Hq % Hkv != 0:
+        raise ValueError("Hq must be a positive multiple of Hkv")
+    return hq // (Hq // Hkv)
+
+
+def visible_mask(Nq, Nk, causal, rows=None):
+    """Boolean (len(rows), Nk) mask of the key positions each query sees.
+
+    Non-causal: every key. Causal (top-left): key j is visible to query i
+    iff j <= i. ``rows`` selects query indices (default: all Nq).
+    """
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    if causal:
+        return j[None, :] <= i[:, None]
+    return np.ones((i.shape[0], Nk), dtype=bool)
+
+
+def scores(q_rows, k_rows, scale):
+    """Scaled scores s_ij = scale * <q_i, k_j> for (n, d) and (m, d) inputs.
+
+    FlashAttention: Part 2, section 2.1: the argument of the softmax is
+    Q K^T scaled (by 1/sqrt(d) by default; here by the caller's scale).
+    """
+    return float(scale) * (_f64(q_rows) @ _f64(k_rows).T)
+
+
+def softmax_rows(S, mask):
+    """Row softmax over visible entries; returns (P, LSE) in float64.
+
+    P_ij = e^(s_ij - LSE_i) on visible entries and 0 elsewhere, with
+    LSE_i = ln sum_{visible j} e^(s_ij) computed as max + ln(sum e^(s - max)).
+    A row with no visible entry gets P = 0 and LSE = -inf.
+    """
+    S = _f64(S)
+    Sm = np.where(mask, S, -np.inf)
+    row_max = Sm.max(axis=1, keepdims=True) if S.shape[1] > 0 else np.full((S.shape[0], 1), -np.inf)
+    empty = ~np.isfinite(row_max)
+    safe_max = np.where(empty, 0.0, row_max)
+    E = np.where(mask, np.exp(Sm - safe_max), 0.0)
+    denom = E.sum(axis=1, keepdims=True)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        P = np.where(empty, 0.0, E / np.where(empty, 1.0, denom))
+        lse = np.where(empty, -np.inf, safe_max + np.log(np.where(empty, 1.0, denom)))
+    return P, lse[:, 0]
+
+
+def attention_rows(q, k, v, causal, scale, b, hq, rows=None):
+    """O and LSE for query head ``hq`` of batch ``b`` at the given rows.
+
+    q: (B, Nq, Hq, d); k, v: (B, Nk, Hkv, d). Returns (O (n, d), LSE (n,)).
+    The full score row block is materialised, masked, softmaxed and
+    multiplied by V (the naive execution the method avoids).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    _, Nq, Hq, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    kv = kv_head_of(hq, Hq, Hkv)
+    rows = np.arange(Nq) if rows is None else np.asarray(rows)
+    S = scores(q[b, rows, hq, :], k[b, :, kv, :], scale)
+    P, lse = softmax_rows(S, visible_mask(Nq, Nk, causal, rows))
+    O = P @ _f64(v[b, :, kv, :])
+    return O, lse
+
+
+def attention(q, k, v, causal, scale):
+    """Full attention: O (B, Nq, Hq, dv) float64 and LSE (B, Hq, Nq) float64."""
+    q = np.asarray(q)
+    B, Nq, Hq, _ = q.shape
+    dv = np.asarray(v).shape[3]
+    O = np.zeros((B, Nq, Hq, dv), dtype=np.float64)
+    L = np.zeros((B, Hq, Nq), dtype=np.float64)
+    for b in range(B):
+        for hq in range(Hq):
+            o, lse = attention_rows(q, k, v, causal, scale, b, hq)
+            O[b, :, hq, :] = o
+            L[b, hq, :] = lse
+    return O, L
+
+
+def decode(q, kcache, vcache, seqlens, scale, heads=None):
+    """One new query per sequence against the first ``seqlens[b]`` cache rows.
+
+    FlashAttention: Part 2, section 4.1: decode has one query row and reads
+    the whole existing cache. q: (B, 1, Hq, d) or (B, Hq, d);
+    kcache, vcache: (B, capacity, Hkv, d); seqlens: (B,) integers.
+    Returns O (B, Hq, dv) and LSE (B, Hq); optional ``heads`` restricts the
+    query heads computed (others are left as NaN).
+    """
+    q = np.asarray(q)
+    if q.ndim == 4:
+        q = q[:, 0]
+    B, Hq, _ = q.shape
+    Hkv = np.asarray(kcache).shape[2]
+    dv = np.asarray(vcache).shape[3]
+    O = np.full((B, Hq, dv), np.nan)
+    L = np.full((B, Hq), np.nan)
+    heads = range(Hq) if heads is None else heads
+    for b in range(B):
+        n = int(seqlens[b])
+        for hq in heads:
+            kv = kv_head_of(hq, Hq, Hkv)
+            S = scores(q[b, hq][None, :], np.asarray(kcache)[b, :n, kv, :], scale)
+            P, lse = softmax_rows(S, np.ones((1, n), dtype=bool))
+            O[b, hq] = (P @ _f64(np.asarray(vcache)[b, :n, kv, :]))[0]
+            L[b, hq] = lse[0]
+    return O, L
+
+
+def merge_partials(o_parts, lse_parts):
+    """Combine results over disjoint key sets into the result over their union.
+
+    pyshine.com FlashAttention code tour, "Why You Need This": decode splits
+    the cache across thread blocks and combines partial results. The combine
+    is not printed; with the per-row log-sum-exp of FlashAttention: Part 2,
+    section 1.3, the exact combine of parts s is
+        LSE = ln sum_s e^(LSE_s),  O = sum_s e^(LSE_s - LSE) O_s.
+    o_parts: (S, ..., d); lse_parts: (S, ...). Parts with LSE = -inf carry no
+    weight; if every part is empty the result is O = 0, LSE = -inf.
+    """
+    o_parts = _f64(o_parts)
+    lse_parts = _f64(lse_parts)
+    m = lse_parts.max(axis=0)
+    empty = ~np.isfinite(m)
+    m_safe = np.where(empty, 0.0, m)
+    w = np.exp(lse_parts - m_safe[None])
+    tot = w.sum(axis=0)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        lse = np.where(empty, -np.inf, m_safe + np.log(np.where(empty, 1.0, tot)))
+        O = (w[..., None] * o_parts).sum(axis=0) / np.where(empty, 1.0, tot)[..., None]
+    O = np.where(empty[..., None], 0.0, O)
+    return O, lse
+
+
+def online_softmax_attention(q_rows, k_rows, v_rows, causal, scale, block_q, block_k):
+    """The tiled online-softmax recurrence, one (batch, head) at a time.
+
+    FlashAttention: Part 2, section 6.2: Q is split into tiles Q_i and K, V
+    into tiles K_j, V_j; for each score tile the state (m, l, a) = (running
+    maximum, running sum of exponentials, running unnormalised value sum) is
+    updated, the old state rescaled by alpha = e^(m - m') when the maximum
+    grows, and the tile discarded. The update equations are lost in the
+    page's text; the plainest recurrence consistent with that state is
+        m' = max(m, rowmax S_ij)
+        l' = e^(m - m') l + sum_j e^(S_ij - m')
+        a' = e^(m - m') a + e^(S_ij - m') V_j
+    and at the end O = a / l and LSE = m + ln l (deferred normalisation,
+    FlashAttention: Part 2, section 1.3 and the post on tracing
+    FlashAttention's evolution through plain PyTorch code).
+    q_rows: (Nq, d); k_rows, v_rows: (Nk, d). Returns (O, LSE).
+    """
+    Q = _f64(q_rows)
+    K = _f64(k_rows)
+    V = _f64(v_rows)
+    Nq, Nk = Q.shape[0], K.shape[0]
+    O = np.zeros((Nq, V.shape[1]))
+    LSE = np.full(Nq, -np.inf)
+    for i0 in range(0, Nq, block_q):
+        rows = np.arange(i0, min(i0 + block_q, Nq))
+        m = np.full(rows.shape[0], -np.inf)
+        l = np.zeros(rows.shape[0])
+        a = np.zeros((rows.shape[0], V.shape[1]))
+        for j0 in range(0, Nk, block_k):
+            cols = np.arange(j0, min(j0 + block_k, Nk))
+            S = scores(Q[rows], K[cols], scale)
+            vis = visible_mask(Nq, Nk, causal, rows)[:, cols]
+            S = np.where(vis, S, -np.inf)
+            m_new = np.maximum(m, S.max(axis=1))
+            m_use = np.where(np.isfinite(m_new), m_new, 0.0)
+            alpha = np.exp(m - m_use)
+            E = np.exp(S - m_use[:, None])
+            l = alpha * l + E.sum(axis=1)
+            a = alpha[:, None] * a + E @ V[cols]
+            m = m_new
+        done = l > 0
+        with np.errstate(divide="ignore", invalid="ignore"):
+            O[rows] = np.where(done[:, None], a / np.where(done, l, 1.0)[:, None], 0.0)
+            LSE[rows] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
+    return O, LSE

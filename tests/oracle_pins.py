@@ -1,0 +1,265 @@
+"""Pins that tie the oracle to something other than itself.
+
+Each ``pin_*`` function raises AssertionError when the oracle disagrees with
+an independent source: a pure-Python brute force on tiny inputs (math.fsum,
+math.exp), a library routine (scipy.special, PyTorch CPU float64
+scaled_dot_product_attention), a closed form, or an invariant the
+definition implies. ``tests/test_oracle.py`` runs them against the real
+oracle; ``tests/test_oracle_mutations.py`` plants plausible mistakes in the
+oracle and checks that some pin fails for each.
+
+Functions are looked up on ``oracle.sdpa`` at call time so a planted mistake
+in any helper reaches every caller.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+from oracle import sdpa as O
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# independent pure-Python brute force (no numpy arithmetic)
+# ---------------------------------------------------------------------------
+def brute_attention(q, k, v, causal, scale):
+    """Triple loop over (batch, query head, query); exact sums via math.fsum."""
+    q = np.asarray(q, dtype=np.float64).tolist()
+    k = np.asarray(k, dtype=np.float64).tolist()
+    v = np.asarray(v, dtype=np.float64).tolist()
+    B, Nq, Hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Nk, Hkv, dv = len(k[0]), len(k[0][0]), len(v[0][0][0])
+    out = np.zeros((B, Nq, Hq, dv))
+    lse = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if (not causal) or j <= i]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = [scale * math.fsum(q[b][i][h][t] * k[b][j][g][t] for t in range(d)) for j in keys]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                den = math.fsum(e)
+                lse[b, h, i] = mx + math.log(den)
+                for t in range(dv):
+                    out[b, i, h, t] = math.fsum(e[n] * v[b][j][g][t] for n, j in enumerate(keys)) / den
+    return out, lse
+
+
+def rng_case(seed, B, Nq, Nk, Hq, Hkv, d, std=1.0):
+    r = np.random.default_rng(seed)
+    q = r.normal(0.0, std, (B, Nq, Hq, d))
+    k = r.normal(0.0, std, (B, Nk, Hkv, d))
+    v = r.normal(0.0, 1.0, (B, Nk, Hkv, d))
+    return q, k, v
+
+
+TINY_SHAPES = [
+    # (B, Nq, Nk, Hq, Hkv, d)
+    (1, 5, 5, 1, 1, 3),
+    (2, 4, 7, 2, 2, 4),
+    (1, 8, 8, 4, 2, 2),
+    (2, 3, 6, 6, 3, 3),
+    (1, 7, 3, 4, 1, 4),
+    (1, 6, 6, 2, 1, 1),
+]
+
+
+def pin_brute_force(tol=1e-12):
+    for n, (B, Nq, Nk, Hq, Hkv, d) in enumerate(TINY_SHAPES):
+        for causal in (False, True):
+            q, k, v = rng_case(100 + n, B, Nq, Nk, Hq, Hkv, d, std=1.5)
+            scale = 1.0 / math.sqrt(d) * 1.3
+            o_ref, l_ref = brute_attention(q, k, v, causal, scale)
+            o, l = O.attention(q, k, v, causal, scale)
+            assert np.max(np.abs(o - o_ref)) <= tol, ("O vs brute force", causal, (B, Nq, Nk, Hq, Hkv, d))
+            assert np.max(np.abs(l - l_ref)) <= tol, ("LSE vs brute force", causal, (B, Nq, Nk, Hq, Hkv, d))
+
+
+def pin_torch_sdpa(tol=1e-12):
+    """PyTorch CPU float64 scaled_dot_product_attention (is_causal is top-left,
+    enable_gqa repeats each KV head over a contiguous block of query heads)."""
+    import torch
+    import torch.nn.functional as F
+    for n, (B, Nq, Nk, Hq, Hkv, d) in enumerate([(2, 9, 9, 4, 2, 8), (1, 16, 16, 8, 2, 16),
+                                                 (1, 5, 12, 3, 3, 4), (2, 12, 12, 2, 1, 5)]):
+        for causal in (False, True):
+            q, k, v = rng_case(200 + n, B, Nq, Nk, Hq, Hkv, d)
+            scale = 0.37
+            o, _ = O.attention(q, k, v, causal, scale)
+            tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x.transpose(0, 2, 1, 3))) for x in (q, k, v))
+            ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=scale,
+                                                 enable_gqa=(Hq != Hkv))
+            ref = ref.numpy().transpose(0, 2, 1, 3)
+            assert np.max(np.abs(o - ref)) <= tol, ("O vs torch SDPA", causal, (B, Nq, Nk, Hq, Hkv, d))
+
+
+def pin_scipy_rows(tol=1e-12):
+    from scipy.special import logsumexp, softmax
+    q, k, v = rng_case(300, 1, 10, 13, 1, 1, 6, std=3.0)
+    scale = 0.8
+    S = scale * np.einsum("id,jd->ij", q[0, :, 0], k[0, :, 0])
+    o, l = O.attention(q, k, v, False, scale)
+    assert np.max(np.abs(l[0, 0] - logsumexp(S, axis=1))) <= tol, "LSE vs scipy logsumexp"
+    assert np.max(np.abs(o[0, :, 0] - softmax(S, axis=1) @ v[0, :, 0])) <= tol, "O vs scipy softmax"
+
+
+def pin_golden_closed_forms(tol=1e-13):
+    with open(os.path.join(GOLDEN, "closed_forms.json")) as f:
+        fixtures = json.load(f)["fixtures"]
+    env = {"e": math.e, "log": math.log, "exp": math.exp, "tanh": math.tanh}
+    for fx in fixtures:
+        q, k, v = (np.array(fx[n], dtype=np.float64) for n in ("q", "k", "v"))
+        o, l = O.attention(q, k, v, fx["causal"], fx["scale"])
+        for ent in fx["o"]:
+            want = eval(ent["expr"], {"__builtins__": {}}, env)  # noqa: S307 - fixed local expressions
+            assert abs(want - ent["value"]) <= 1e-15 * max(1.0, abs(want)), ("fixture typo", fx["name"])
+            assert abs(o[tuple(ent["index"])] - want) <= tol, ("golden O", fx["name"], ent["index"])
+        for ent in fx["lse"]:
+            want = eval(ent["expr"], {"__builtins__": {}}, env)  # noqa: S307
+            assert abs(want - ent["value"]) <= 1e-15 * max(1.0, abs(want)), ("fixture typo", fx["name"])
+            assert abs(l[tuple(ent["index"])] - want) <= tol, ("golden LSE", fx["name"], ent["index"])
+
+
+def pin_row_stochastic(tol=1e-12):
+    q, k, _ = rng_case(400, 1, 12, 12, 1, 1, 5, std=2.0)
+    for causal in (False, True):
+        S = O.scores(q[0, :, 0], k[0, :, 0], 0.7)
+        P, _ = O.softmax_rows(S, O.visible_mask(12, 12, causal))
+        assert np.all(P >= 0.0), "P negative"
+        assert np.max(np.abs(P.sum(axis=1) - 1.0)) <= tol, "rows of P do not sum to 1"
+        if causal:
+            assert np.all(P[np.triu_indices(12, 1)] == 0.0), "causal P leaks future keys"
+
+
+def pin_constant_values(tol=1e-12):
+    q, k, v = rng_case(500, 2, 9, 9, 4, 2, 3, std=2.0)
+    c = np.array([1.25, -3.0, 0.5])
+    v[:] = c
+    for causal in (False, True):
+        o, _ = O.attention(q, k, v, causal, 0.9)
+        assert np.max(np.abs(o - c)) <= tol, "constant V not reproduced"
+
+
+def pin_key_permutation(tol=1e-12):
+    q, k, v = rng_case(600, 1, 6, 11, 2, 1, 4)
+    perm = np.random.default_rng(601).permutation(11)
+    o1, l1 = O.attention(q, k, v, False, 0.6)
+    o2, l2 = O.attention(q, k[:, perm], v[:, perm], False, 0.6)
+    assert np.max(np.abs(o1 - o2)) <= tol and np.max(np.abs(l1 - l2)) <= tol, "not key-permutation equivariant"
+
+
+def pin_zero_query_closed_form(tol=1e-12):
+    _, k, v = rng_case(700, 1, 7, 7, 2, 2, 3)
+    q = np.zeros((1, 7, 2, 3))
+    for causal in (False, True):
+        o, l = O.attention(q, k, v, causal, 1.0)
+        for i in range(7):
+            n = i + 1 if causal else 7
+            assert np.max(np.abs(o[0, i] - v[0, :n].mean(axis=0))) <= tol, ("q=0 mean", causal, i)
+            assert np.max(np.abs(l[0, :, i] - math.log(n))) <= tol, ("q=0 LSE", causal, i)
+
+
+def pin_single_key(tol=1e-12):
+    q, k, v = rng_case(800, 2, 4, 1, 2, 1, 5)
+    for causal in (False, True):
+        o, l = O.attention(q, k, v, causal, 0.45)
+        for h in range(2):
+            assert np.max(np.abs(o[:, :, h] - v[:, 0:1, 0])) <= tol, "Nk=1: O != v0"
+            s = 0.45 * np.einsum("bnd,bd->bn", q[:, :, h], k[:, 0, 0])
+            assert np.max(np.abs(l[:, h] - s)) <= tol, "Nk=1: LSE != s00"
+
+
+def pin_large_scale_argmax(tol=1e-9):
+    q, k, v = rng_case(900, 1, 5, 8, 1, 1, 4)
+    o, _ = O.attention(q, k, v, False, 1.0e4)
+    S = q[0, :, 0] @ k[0, :, 0].T
+    assert np.max(np.abs(o[0, :, 0] - v[0, S.argmax(axis=1), 0])) <= tol, "hard-max limit"
+
+
+def pin_causal_prefix(tol=1e-12):
+    q, k, v = rng_case(1000, 1, 8, 8, 2, 2, 3)
+    oc, lc = O.attention(q, k, v, True, 0.5)
+    for i in range(8):
+        on, ln = O.attention(q[:, i:i + 1], k[:, :i + 1], v[:, :i + 1], False, 0.5)
+        assert np.max(np.abs(oc[:, i:i + 1] - on)) <= tol and np.max(np.abs(lc[:, :, i:i + 1] - ln)) <= tol, (
+            "causal row i != full attention over keys 0..i", i)
+
+
+def pin_gqa_repeat(tol=1e-15):
+    q, k, v = rng_case(1100, 2, 6, 6, 6, 2, 3)
+    for causal in (False, True):
+        o1, l1 = O.attention(q, k, v, causal, 0.7)
+        o2, l2 = O.attention(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), causal, 0.7)
+        assert np.max(np.abs(o1 - o2)) <= tol and np.max(np.abs(l1 - l2)) <= tol, "GQA != repeat-interleaved MHA"
+
+
+def pin_split_combine(tol=1e-12):
+    """Parts over disjoint key sets, each from the brute force, merge to the full result."""
+    q, k, v = rng_case(1200, 1, 5, 13, 2, 1, 4)
+    o_full, l_full = brute_attention(q, k, v, False, 0.8)
+    cuts = [0, 4, 4, 9, 13]  # includes an empty part
+    parts_o, parts_l = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        if b > a:
+            po, pl = brute_attention(q, k[:, a:b], v[:, a:b], False, 0.8)
+        else:
+            po, pl = np.zeros_like(o_full), np.full_like(l_full, -np.inf)
+        parts_o.append(po)
+        parts_l.append(pl.transpose(0, 2, 1))  # (B, Nq, Hq) to match O's leading dims
+    o, l = O.merge_partials(np.stack(parts_o), np.stack(parts_l))
+    assert np.max(np.abs(o - o_full)) <= tol, "merged O != full"
+    assert np.max(np.abs(l - l_full.transpose(0, 2, 1))) <= tol, "merged LSE != full"
+    o0, l0 = O.merge_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(o0 == 0.0) and np.all(l0 == -np.inf), "all-empty merge"
+
+
+def pin_decode(tol=1e-12):
+    r = np.random.default_rng(1300)
+    B, cap, Hq, Hkv, d = 3, 9, 4, 2, 5
+    q = r.normal(size=(B, 1, Hq, d))
+    kc = r.normal(size=(B, cap, Hkv, d))
+    vc = r.normal(size=(B, cap, Hkv, d))
+    lens = [1, 9, 4]
+    o, l = O.decode(q, kc, vc, lens, 0.45)
+    for b, n in enumerate(lens):
+        ob, lb = brute_attention(q[b:b + 1], kc[b:b + 1, :n], vc[b:b + 1, :n], False, 0.45)
+        assert np.max(np.abs(o[b] - ob[0, 0])) <= tol, ("decode O", b)
+        assert np.max(np.abs(l[b] - lb[0, :, 0])) <= tol, ("decode LSE", b)
+
+
+def pin_online_recurrence(tol=1e-12):
+    """The tiled (m, l, a) recurrence reaches the brute-force result."""
+    q, k, v = rng_case(1400, 1, 11, 11, 1, 1, 4, std=3.0)
+    for causal in (False, True):
+        ob, lb = brute_attention(q, k, v, causal, 0.9)
+        for bq, bk in ((4, 3), (11, 11), (1, 5)):
+            o, l = O.online_softmax_attention(q[0, :, 0], k[0, :, 0], v[0, :, 0], causal, 0.9, bq, bk)
+            assert np.max(np.abs(o - ob[0, :, 0])) <= tol, ("recurrence O", causal, bq, bk)
+            assert np.max(np.abs(l - lb[0, 0])) <= tol, ("recurrence LSE", causal, bq, bk)
+
+
+ALL_PINS = [
+    pin_brute_force,
+    pin_torch_sdpa,
+    pin_scipy_rows,
+    pin_golden_closed_forms,
+    pin_row_stochastic,
+    pin_constant_values,
+    pin_key_permutation,
+    pin_zero_query_closed_form,
+    pin_single_key,
+    pin_large_scale_argmax,
+    pin_causal_prefix,
+    pin_gqa_repeat,
+    pin_split_combine,
+    pin_decode,
+    pin_online_recurrence,
+]

@@ -1,0 +1,149 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin fails.
+
+Each mutation replaces one helper of ``oracle.sdpa`` for the duration of the
+test; the pin suite must reject every one of them, which shows the pins
+constrain each part of the oracle rather than echo it.
+"""
+
+import numpy as np
+import pytest
+
+import oracle_pins as P
+from oracle import sdpa as O
+
+_orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
+                                    "attention_rows", "decode", "merge_partials",
+                                    "online_softmax_attention")}
+
+
+def _interleaved_groups(hq, Hq, Hkv):
+    _orig["kv_head_of"](hq, Hq, Hkv)
+    return hq % Hkv
+
+
+def _strict_causal(Nq, Nk, causal, rows=None):
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    return (j[None, :] < i[:, None]) if causal else np.ones((i.shape[0], Nk), dtype=bool)
+
+
+def _reversed_causal(Nq, Nk, causal, rows=None):
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    return (j[None, :] >= i[:, None]) if causal else np.ones((i.shape[0], Nk), dtype=bool)
+
+
+def _bottom_right_causal(Nq, Nk, causal, rows=None):
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    return (j[None, :] <= i[:, None] + (Nk - Nq)) if causal else np.ones((i.shape[0], Nk), dtype=bool)
+
+
+def _no_scale(q_rows, k_rows, scale):
+    return _orig["scores"](q_rows, k_rows, 1.0)
+
+
+def _sqrt_scale(q_rows, k_rows, scale):
+    return _orig["scores"](q_rows, k_rows, scale / np.sqrt(np.asarray(q_rows).shape[-1]))
+
+
+def _transposed_scores(q_rows, k_rows, scale):
+    S = _orig["scores"](q_rows, k_rows, scale)
+    return S.T if S.shape[0] == S.shape[1] else S[:, ::-1]
+
+
+def _lse_without_max(S, mask):
+    P_, lse = _orig["softmax_rows"](S, mask)
+    S = np.where(mask, np.asarray(S, float), -np.inf)
+    mx = S.max(axis=1)
+    return P_, lse - np.where(np.isfinite(mx), mx, 0.0)
+
+
+def _unnormalised(S, mask):
+    P_, lse = _orig["softmax_rows"](S, mask)
+    return P_ * np.exp(lse)[:, None] / np.exp(np.where(np.isfinite(lse), lse.max(), 0.0)), lse
+
+
+def _column_softmax(S, mask):
+    P_, lse = _orig["softmax_rows"](np.asarray(S).T, np.asarray(mask).T)
+    if P_.shape[0] != P_.shape[1]:
+        return _orig["softmax_rows"](S, mask)[0][:, ::-1], lse[: np.asarray(S).shape[0]]
+    return P_.T, lse
+
+
+def _values_from_keys(q, k, v, causal, scale, b, hq, rows=None):
+    return _orig["attention_rows"](q, k, k if np.asarray(k).shape == np.asarray(v).shape else v,
+                                   causal, scale, b, hq, rows)
+
+
+def _decode_off_by_one(q, kcache, vcache, seqlens, scale, heads=None):
+    cap = np.asarray(kcache).shape[1]
+    return _orig["decode"](q, kcache, vcache, [min(int(n) + 1, cap) if int(n) < cap else int(n) - 1
+                                               for n in seqlens], scale, heads)
+
+
+def _merge_plain_mean(o_parts, lse_parts):
+    o, lse = _orig["merge_partials"](o_parts, lse_parts)
+    return np.asarray(o_parts, float).mean(axis=0), lse
+
+
+def _recurrence_wrong_alpha(q_rows, k_rows, v_rows, causal, scale, block_q, block_k):
+    # alpha = e^(m' - m) instead of e^(m - m'): emulate by running the
+    # recurrence with the opposite rescale through a local copy.
+    Q, K, V = (np.asarray(x, float) for x in (q_rows, k_rows, v_rows))
+    Nq, Nk = Q.shape[0], K.shape[0]
+    Oo = np.zeros((Nq, V.shape[1]))
+    L = np.zeros(Nq)
+    for i0 in range(0, Nq, block_q):
+        rows = np.arange(i0, min(i0 + block_q, Nq))
+        m = np.full(len(rows), -np.inf)
+        l = np.zeros(len(rows))
+        a = np.zeros((len(rows), V.shape[1]))
+        for j0 in range(0, Nk, block_k):
+            cols = np.arange(j0, min(j0 + block_k, Nk))
+            S = scale * Q[rows] @ K[cols].T
+            if causal:
+                S = np.where(cols[None, :] <= rows[:, None], S, -np.inf)
+            m_new = np.maximum(m, S.max(axis=1))
+            mu = np.where(np.isfinite(m_new), m_new, 0.0)
+            alpha = np.where(np.isfinite(m), np.exp(np.minimum(mu - m, 50.0)), 0.0)
+            E = np.exp(S - mu[:, None])
+            l = alpha * l + E.sum(axis=1)
+            a = alpha[:, None] * a + E @ V[cols]
+            m = m_new
+        Oo[rows] = a / l[:, None]
+        L[rows] = m + np.log(l)
+    return Oo, L
+
+
+MUTATIONS = [
+    ("kv_head_of", _interleaved_groups),
+    ("visible_mask", _strict_causal),
+    ("visible_mask", _reversed_causal),
+    ("visible_mask", _bottom_right_causal),
+    ("scores", _no_scale),
+    ("scores", _sqrt_scale),
+    ("scores", _transposed_scores),
+    ("softmax_rows", _lse_without_max),
+    ("softmax_rows", _unnormalised),
+    ("softmax_rows", _column_softmax),
+    ("attention_rows", _values_from_keys),
+    ("decode", _decode_off_by_one),
+    ("merge_partials", _merge_plain_mean),
+    ("online_softmax_attention", _recurrence_wrong_alpha),
+]
+
+
+@pytest.mark.parametrize("name,bad", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
+def test_some_pin_rejects_mutation(monkeypatch, name, bad):
+    monkeypatch.setattr(O, name, bad)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as exc:  # a crash also counts as caught, but say so
+            failed.append(f"{pin.__name__}({type(exc).__name__})")
+    assert failed, f"no pin caught the planted mistake {name}:{bad.__name__}"
