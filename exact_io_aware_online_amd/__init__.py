@@ -1,0 +1,189 @@
+"""Exact IO-aware attention for MI355X (gfx950): Python binding of libfa.so.
+
+The binding only marshals arguments: it checks dtypes, devices and
+contiguity, takes raw device pointers and the current HIP stream from torch
+tensors, and calls the C ABI of ``include/fa.h`` through ctypes. Every step
+of the computation runs in the HIP kernels of ``libfa.so``; there is no
+fallback, and calling anything here without the built library raises.
+"""
+
+import ctypes
+import math
+import os
+
+__all__ = [
+    "FAError",
+    "lib",
+    "fa_abi_version",
+    "fa_status_string",
+    "fa_fwd",
+    "fa_fwd_kvcache",
+    "fa_fwd_kvcache_workspace_size",
+    "fa_kvcache_default_splits",
+    "FA_DTYPE_BF16",
+    "FA_DTYPE_F32",
+]
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = range(5)
+FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {fa_status_string(status)} (status {status})")
+
+
+def lib():
+    """The loaded libfa.so (ctypes.CDLL); raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with `python -m exact_io_aware_online_amd.build` "
+                          "(there is no fallback implementation)")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.fa_abi_version.restype = i
+    L.fa_abi_version.argtypes = []
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_status_string.argtypes = [i]
+    L.fa_fwd.restype = i
+    L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.fa_fwd_kvcache.restype = i
+    L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_fwd_kvcache_workspace_size.restype = sz
+    L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
+    L.fa_kvcache_default_splits.restype = i
+    L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i]
+    _lib = L
+    return L
+
+
+def fa_abi_version():
+    return lib().fa_abi_version()
+
+
+def fa_status_string(status):
+    return lib().fa_status_string(int(status)).decode()
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtype=None, device=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None, want_lse=True):
+    """Attention forward through ``fa_fwd``.
+
+    q: (B, Nq, Hq, d); k, v: (B, Nk, Hkv, d); bf16 or float32, contiguous,
+    on one GPU. ``o`` (like q) and ``lse`` ((B, Hq, Nq) float32) are
+    allocated when not given. Returns (o, lse); lse is None when
+    ``want_lse`` is false and no ``lse`` tensor was passed.
+    """
+    import torch
+    if q.dtype == torch.bfloat16:
+        dt = FA_DTYPE_BF16
+    elif q.dtype == torch.float32:
+        dt = FA_DTYPE_F32
+    else:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be (batch, seq, heads, head_dim)")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Nk, Hkv, d) or tuple(v.shape) != (B, Nk, Hkv, d):
+        raise ValueError(f"k/v shapes {tuple(k.shape)}/{tuple(v.shape)} do not match q {tuple(q.shape)}")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, q.dtype, q.device)
+    if o is None:
+        o = torch.empty_like(q)
+    _check(o, "o", q.dtype, q.device)
+    if tuple(o.shape) != tuple(q.shape):
+        raise ValueError("o must have q's shape")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+        if tuple(lse.shape) != (B, Hq, Nq):
+            raise ValueError("lse must be (B, Hq, Nq)")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                      int(bool(causal)), float(scale), dt, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits):
+    return int(lib().fa_fwd_kvcache_workspace_size(int(B), int(Hq), int(d), int(num_splits)))
+
+
+def fa_kvcache_default_splits(B, Hkv, capacity, num_cus=0, wgs_per_cu=0):
+    return int(lib().fa_kvcache_default_splits(int(B), int(Hkv), int(capacity), int(num_cus), int(wgs_per_cu)))
+
+
+def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_splits=None, scale=None,
+                   workspace=None, stream=None, want_lse=True):
+    """Split-KV decode through ``fa_fwd_kvcache``.
+
+    q: (B, 1, Hq, d) bf16; kcache, vcache: (B, capacity, Hkv, d) bf16;
+    cache_seqlens: (B,) int32 on the same GPU. ``num_splits`` defaults to
+    ``fa_kvcache_default_splits``; the workspace is allocated when needed
+    and not given. Returns (o (B, 1, Hq, d) bf16, lse (B, Hq) float32).
+    """
+    import torch
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be (batch, 1, heads, head_dim)")
+    B, _, Hq, d = q.shape
+    _, cap, Hkv, dk = kcache.shape
+    if dk != d or tuple(vcache.shape) != tuple(kcache.shape) or kcache.shape[0] != B:
+        raise ValueError("cache shapes do not match q")
+    for t, n in ((q, "q"), (kcache, "kcache"), (vcache, "vcache")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, q.device)
+    if tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("cache_seqlens must be (B,)")
+    if num_splits is None:
+        num_splits = fa_kvcache_default_splits(B, Hkv, cap)
+    if o is None:
+        o = torch.empty_like(q)
+    _check(o, "o", torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+    need = fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_kvcache(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
+                              int(num_splits), B, Hq, Hkv, cap, d, float(scale), _ptr(workspace), ws_bytes,
+                              _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache")
+    return o, lse

@@ -1,0 +1,137 @@
+// fa_api.cpp - the C ABI declared in include/fa.h.
+//
+// Host-side shape policing before any launch (pyshine.com FlashAttention
+// code tour, "Why You Need This" and the C++ layer described there, which
+// validates strides and head dimensions and dispatches on head dimension).
+// Every check runs before the first HIP call, so a rejected call touches
+// neither the device nor the caller's buffers.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
+
+fa_status_t launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_abi_version(void) { return kAbiVersion; }
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim/dtype/group";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
+    default: return "FA_ERR_UNKNOWN";
+  }
+}
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int dtype, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
+  const bool supported = dtype == FA_DTYPE_BF16 ? fa::fwd_bf16_supported(d) : fa::fwd_f32_supported(d);
+  if (!supported) return FA_ERR_UNSUPPORTED;
+  // grid limits: y = Hq, z = B
+  if (Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
+
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || d <= 0 || num_splits <= 1) return 0;
+  return fa::decode_workspace_bytes(B, Hq, d, num_splits);
+}
+
+int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu) {
+  if (B <= 0 || Hkv <= 0 || capacity <= 0) return 1;
+  if (num_cus <= 0) {
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess) {
+      num_cus = prop.multiProcessorCount;
+    } else {
+      num_cus = 256;
+    }
+  }
+  if (wgs_per_cu <= 0) wgs_per_cu = 2;
+  // Workgroups of about half the splits hold keys when lengths spread over
+  // the capacity, so aim the total at twice the resident target.
+  const long target = 2L * num_cus * wgs_per_cu;
+  const long pairs = (long)B * Hkv;
+  long s = (target + pairs - 1) / pairs;
+  const long max_s = (capacity + 63) / 64;  // at least one 64-key tile per split
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  if (s > 1024) s = 1024;
+  return (int)s;
+}
+
+fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* cache_seqlens, void* o, float* lse,
+                           int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!fa::decode_supported(d, Hq / Hkv)) return FA_ERR_UNSUPPORTED;
+  if (num_splits > 65535 || Hkv > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if (B == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || cache_seqlens == nullptr) return FA_ERR_INVALID_ARG;
+  if (capacity > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_INVALID_ARG;
+  const size_t need = fa::decode_workspace_bytes(B, Hq, d, num_splits);
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+
+  fa::DecodeArgs a;
+  a.q = q;
+  a.kcache = kcache;
+  a.vcache = vcache;
+  a.seqlens = cache_seqlens;
+  a.o = o;
+  a.lse = lse;
+  a.num_splits = num_splits;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.capacity = capacity;
+  a.d = d;
+  a.scale = scale;
+  a.workspace = workspace;
+  return launch_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

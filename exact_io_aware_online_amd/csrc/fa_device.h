@@ -1,0 +1,71 @@
+// fa_device.h - device-side building blocks shared by the gfx950 kernels.
+//
+// MFMA operand layouts used throughout (verified on gfx950 by feeding the
+// instruction known integer matrices and comparing with a host product):
+//   v_mfma_f32_32x32x16_bf16 (lane l, g = l / 32, register i):
+//     A[m][k]: m = l % 32, k = 8 g + i   (i = 0..7)
+//     B[k][n]: n = l % 32, k = 8 g + i   (i = 0..7)
+//     C[m][n]: n = l % 32, m = 8 (i / 4) + 4 g + (i % 4)   (i = 0..15)
+//   v_mfma_f32_16x16x32_bf16 (g = l / 16):
+//     A[m][k]: m = l % 16, k = 8 g + i;  B[k][n]: n = l % 16, k = 8 g + i
+//     C[m][n]: n = l % 16, m = 4 g + i   (i = 0..3)
+//   v_mfma_f32_16x16x16_bf16 (g = l / 16):
+//     A[m][k]: m = l % 16, k = 4 g + i;  B[k][n]: n = l % 16, k = 4 g + i
+//     C[m][n]: n = l % 16, m = 4 g + i
+// Only the pairing of A's and B's k index matters for a product, so any
+// permutation of k applied to both operands gives the same sum.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// log2(e): e^x = 2^(x * log2 e). The kernels keep the running maximum in
+// base-2 units, t = s * scale * log2(e), and use the hardware 2^x.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16(const i16x4& a, const i16x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Two floats -> packed bf16 pair, round-to-nearest-even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 r = {(bf16)lo, (bf16)hi};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Cross-lane exchange with the lane 32 positions away (the other half of a
+// 64-wide wavefront).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ u32x4 load_u32x4(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void store_u32x4(void* p, const u32x4& v) {
+  *reinterpret_cast<u32x4*>(p) = v;
+}
+
+}  // namespace fa

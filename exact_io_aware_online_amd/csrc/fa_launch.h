@@ -1,0 +1,51 @@
+// fa_launch.h - host-side launchers behind the C ABI (internal).
+//
+// The C entry points in fa_api.cpp validate arguments and then call these;
+// each launcher picks the kernel instantiation for the head dimension and
+// enqueues it on the caller's stream. They assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal;
+  float scale;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* kcache;
+  const void* vcache;
+  const int32_t* seqlens;
+  void* o;
+  float* lse;  // may be null
+  int num_splits;
+  int B, Hq, Hkv, capacity, d;
+  float scale;
+  void* workspace;  // >= decode_workspace_bytes(...) when num_splits > 1
+};
+
+// Keys per split for a cache of `capacity` rows cut into `num_splits`
+// pieces: the smallest multiple of the decode key tile >= ceil(cap / S).
+int decode_chunk(int capacity, int num_splits);
+size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits);
+
+bool fwd_bf16_supported(int d);
+bool fwd_f32_supported(int d);
+bool decode_supported(int d, int group);
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace fa

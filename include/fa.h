@@ -1,0 +1,138 @@
+/*
+ * fa.h - C ABI of the exact IO-aware attention library (libfa.so), gfx950.
+ *
+ * What it computes. Exact scaled-dot-product attention forward,
+ *     O = softmax(scale * Q K^T) V,  LSE_i = ln sum_{visible j} e^(scale <q_i, k_j>),
+ * evaluated as tiled online softmax: score tiles live only in registers and
+ * the N x N score matrix never reaches device memory
+ * (FlashAttention: Part 2, section 2.1 for the function; section 6.2
+ * "FlashAttention Summary" for the tile -> score -> online softmax -> V
+ * accumulation -> discard pipeline; section 1.3 for the one log-sum-exp per
+ * query row kept next to the output; section 1.2 for one workgroup per
+ * query-row tile).
+ *
+ * Conventions shared by every entry point.
+ *  - Pointers: every tensor pointer is a DEVICE pointer (HIP device memory)
+ *    owned by the caller. The library never allocates, frees or
+ *    synchronises; it only enqueues kernels on `stream`.
+ *  - stream: a hipStream_t passed as void*; NULL means the null stream.
+ *    Calls return as soon as the kernels are enqueued; results are ready
+ *    once the stream reaches them. Device faults surface at the caller's
+ *    next synchronisation.
+ *  - Layout: dense, contiguous, row-major (batch, sequence, heads, head_dim)
+ *    for q, k, v, o and the caches; lse is (batch, heads, queries) float32.
+ *  - Grouped heads (pyshine.com FlashAttention code tour, "Why You Need
+ *    This": K and V may carry fewer heads than Q when the counts divide):
+ *    Hq must be a positive multiple of Hkv, and query head h reads key/value
+ *    head h / (Hq / Hkv) (contiguous groups).
+ *  - Errors: arguments are checked on the host before anything is
+ *    enqueued; on any error nothing is written and a non-zero fa_status_t
+ *    is returned. FA_ERR_LAUNCH reports a failed kernel launch.
+ *  - Thread safety: the library keeps no mutable state; concurrent calls
+ *    on different streams are safe.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, Hq % Hkv != 0, bad scale */
+  FA_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for */
+  FA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
+  FA_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch */
+} fa_status_t;
+
+typedef enum {
+  FA_DTYPE_BF16 = 0, /* bfloat16 in/out; bf16 MFMA products, fp32 accumulation */
+  FA_DTYPE_F32 = 1   /* float32 in/out; fp32 products and accumulation */
+} fa_dtype_t;
+
+/* Version of this ABI (bumped on any incompatible change). */
+int fa_abi_version(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/*
+ * fa_fwd - prefill / training forward.
+ *
+ * q   : (B, Nq, Hq, d) of `dtype`.
+ * k, v: (B, Nk, Hkv, d) of `dtype`.
+ * o   : (B, Nq, Hq, d) of `dtype`, written.
+ * lse : (B, Hq, Nq) float32, written (natural-log units of the scaled
+ *       scores); may be NULL when the caller does not need it.
+ * causal: 0 = every key visible; 1 = top-left causal, key j is visible to
+ *       query i iff j <= i (pyshine.com FlashAttention code tour, "From
+ *       Install to Causal Attention"; for Nq == Nk top-left and bottom-right
+ *       alignment coincide).
+ * scale: multiplies q.k before the softmax; must be finite and > 0
+ *       (1/sqrt(d) reproduces the usual definition).
+ * d   : 64, 128 or 256 for FA_DTYPE_BF16; 64 for FA_DTYPE_F32.
+ *
+ * B == 0 or Nq == 0 is a no-op. Nk == 0 leaves every row without a visible
+ * key: o = 0 and lse = -inf. Rows never produce NaN from masking.
+ * Returns FA_ERR_INVALID_ARG for a negative size, Hq % Hkv != 0, a null
+ * q/k/v/o pointer with non-zero extent, or a bad scale; FA_ERR_UNSUPPORTED
+ * for an unsupported (dtype, d).
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                   int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_kvcache - split-KV decode: one new query per sequence against a
+ * contiguous key/value cache (pyshine.com FlashAttention code tour, "Why You
+ * Need This": with query length one the cache loading is split across
+ * workgroups and the partial results are combined; FlashAttention: Part 2,
+ * section 4.1: decode reads the cache and is memory-bound).
+ *
+ * q            : (B, 1, Hq, d) bf16.
+ * kcache,vcache: (B, capacity, Hkv, d) bf16; rows at or beyond
+ *                cache_seqlens[b] are never read.
+ * cache_seqlens: (B,) int32 device array; key j of sequence b is visible iff
+ *                j < cache_seqlens[b]. Values are clamped to [0, capacity].
+ * o            : (B, 1, Hq, d) bf16, written.
+ * lse          : (B, Hq) float32, written; may be NULL.
+ * num_splits   : S >= 1. Split s of a sequence covers keys
+ *                [s*c, min((s+1)*c, L_b)) with c = the smallest multiple of
+ *                64 >= ceil(capacity / S); splits that start at or beyond
+ *                L_b do no work. S == 1 writes o directly and needs no
+ *                workspace; S > 1 writes per-split partial (O_s, LSE_s)
+ *                into the workspace and a second kernel combines them with
+ *                log-sum-exp weights.
+ * workspace    : device scratch of at least
+ *                fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits) bytes
+ *                (may be NULL when that size is 0). Contents on entry are
+ *                ignored; calls sharing one workspace must be ordered on
+ *                one stream.
+ * d            : 64, 128 or 256; Hq / Hkv must be at most 16.
+ * L_b == 0 gives o = 0 and lse = -inf for that sequence.
+ */
+fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* cache_seqlens, void* o, float* lse,
+                           int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fa_fwd_kvcache needs for these sizes (0 when
+ * num_splits <= 1); 0 also for invalid sizes. */
+size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
+
+/* A num_splits that gives the decode kernel roughly `wgs_per_cu` resident
+ * workgroups per compute unit for B sequences of at most `capacity` keys
+ * and Hkv key/value heads on a device with `num_cus` compute units
+ * (pass 0 for either to use the current device's count and 2 per CU).
+ * Always >= 1. */
+int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

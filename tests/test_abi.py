@@ -1,0 +1,117 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching the device (CPU only: no call here
+reaches a kernel launch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import exact_io_aware_online_amd as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+# a non-null address that is never dereferenced: every call below fails
+# validation before any pointer is used
+FAKE = ctypes.c_void_p(0x1000)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = fa.lib()
+    names = declared_functions()
+    assert {"fa_fwd", "fa_fwd_kvcache", "fa_fwd_kvcache_workspace_size", "fa_kvcache_default_splits",
+            "fa_status_string", "fa_abi_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libfa.so does not export {n}"
+
+
+def test_status_strings_and_version():
+    assert fa.fa_abi_version() == 1
+    for s in range(5):
+        assert fa.fa_status_string(s).startswith("FA_")
+    assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
+
+
+def _fwd(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, B=1, Hq=4, Hkv=2, Nq=8, Nk=8, d=128,
+             causal=0, scale=0.1, dtype=fa.FA_DTYPE_BF16, stream=None)
+    a.update(kw)
+    return fa.lib().fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                           a["Nk"], a["d"], a["causal"], ctypes.c_float(a["scale"]), a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(Hkv=0), fa.FA_ERR_INVALID_ARG),
+    (dict(B=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(Nq=-3), fa.FA_ERR_INVALID_ARG),
+    (dict(Nk=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=-1.0), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("nan")), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), fa.FA_ERR_INVALID_ARG),
+    (dict(causal=2), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(o=None), fa.FA_ERR_INVALID_ARG),
+    (dict(k=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=96), fa.FA_ERR_UNSUPPORTED),
+    (dict(d=512), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=fa.FA_DTYPE_F32, d=128), fa.FA_ERR_UNSUPPORTED),
+    (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=0), fa.FA_OK),          # no-op, nothing launched
+    (dict(Nq=0), fa.FA_OK),         # no-op, nothing launched
+])
+def test_fwd_host_validation(kw, status):
+    assert _fwd(**kw) == status
+
+
+def _kv(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, lens=FAKE, o=FAKE, lse=None, S=4, B=2, Hq=8, Hkv=2, cap=256, d=128,
+             scale=0.1, ws=FAKE, ws_bytes=1 << 30, stream=None)
+    a.update(kw)
+    return fa.lib().fa_fwd_kvcache(a["q"], a["kc"], a["vc"], a["lens"], a["o"], a["lse"], a["S"], a["B"], a["Hq"],
+                                   a["Hkv"], a["cap"], a["d"], ctypes.c_float(a["scale"]), a["ws"], a["ws_bytes"],
+                                   a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Hq=6, Hkv=4), fa.FA_ERR_INVALID_ARG),
+    (dict(S=0), fa.FA_ERR_INVALID_ARG),
+    (dict(cap=-1), fa.FA_ERR_INVALID_ARG),
+    (dict(scale=0.0), fa.FA_ERR_INVALID_ARG),
+    (dict(lens=None), fa.FA_ERR_INVALID_ARG),
+    (dict(q=None), fa.FA_ERR_INVALID_ARG),
+    (dict(kc=None), fa.FA_ERR_INVALID_ARG),
+    (dict(d=80), fa.FA_ERR_UNSUPPORTED),
+    (dict(Hq=64, Hkv=2), fa.FA_ERR_UNSUPPORTED),   # 32 query heads per KV head
+    (dict(ws=None), fa.FA_ERR_WORKSPACE),
+    (dict(ws_bytes=100), fa.FA_ERR_WORKSPACE),
+    (dict(B=0), fa.FA_OK),
+])
+def test_kvcache_host_validation(kw, status):
+    assert _kv(**kw) == status
+
+
+def test_workspace_size_formula():
+    assert fa.fa_fwd_kvcache_workspace_size(64, 32, 128, 1) == 0
+    assert fa.fa_fwd_kvcache_workspace_size(64, 32, 128, 8) == 64 * 32 * 8 * 129 * 4
+    assert fa.fa_fwd_kvcache_workspace_size(0, 32, 128, 8) == 0
+    # the exact boundary: one byte short is rejected before launch
+    need = fa.fa_fwd_kvcache_workspace_size(2, 8, 128, 4)
+    assert _kv(ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_default_splits():
+    s = fa.fa_kvcache_default_splits(64, 8, 8192, 256, 2)
+    assert 1 <= s <= 8192 // 64
+    assert fa.fa_kvcache_default_splits(1, 1, 64, 256, 2) == 1   # one tile: cannot split
+    assert fa.fa_kvcache_default_splits(4096, 8, 8192, 256, 2) == 1
+    assert fa.fa_kvcache_default_splits(0, 8, 8192, 256, 2) == 1

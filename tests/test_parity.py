@@ -1,0 +1,281 @@
+"""GPU parity: the HIP path through the C ABI against the CPU float64 oracle.
+
+Tolerances (element-wise max-abs error): O <= 2e-2 for bf16, O <= 1e-5 for
+float32, LSE <= 1e-3 for both. Inputs come from ``seeded_inputs``; the
+oracle sees the same (bf16- or fp32-valued) numbers upcast to float64 and
+the exact float32 scale the library receives.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as SI
+from oracle import sdpa as O
+
+pytestmark = pytest.mark.gpu
+
+TOL_O = {"bf16": 2e-2, "f32": 1e-5}
+TOL_LSE = 1e-3
+
+
+def fa():
+    import exact_io_aware_online_amd as m
+    m.lib()
+    return m
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def f32scale(d):
+    return float(np.float32(1.0 / math.sqrt(d)))
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def run_prefill(B, Hq, Hkv, Nq, Nk, d, dtype, causal, seed, std_qk=1.0, std_v=1.0, scale=None):
+    dev = torch.device("cuda")
+    q, k, v = SI.prefill_inputs(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=d, dtype=dtype, seed=seed,
+                                std_qk=std_qk, std_v=std_v, device=dev)
+    scale = f32scale(d) if scale is None else float(np.float32(scale))
+    o, lse = fa().fa_fwd(q, k, v, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    return q, k, v, o, lse, scale
+
+
+def check_full(B, Hq, Hkv, Nq, Nk, d, dtype, causal, seed, std_qk=1.0, std_v=1.0):
+    note(f"prefill B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} d={d} {dtype} causal={causal} seed={seed}")
+    q, k, v, o, lse, scale = run_prefill(B, Hq, Hkv, Nq, Nk, d, dtype, causal, seed, std_qk, std_v)
+    o_ref, l_ref = O.attention(f64(q), f64(k), f64(v), causal, scale)
+    eo = np.max(np.abs(f64(o) - o_ref)) if o_ref.size else 0.0
+    el = np.max(np.abs(f64(lse) - l_ref)) if l_ref.size else 0.0
+    note(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+    assert eo <= TOL_O[dtype], eo
+    assert el <= TOL_LSE, el
+    return q, k, v, o, lse
+
+
+# (B, Hq, Hkv, Nq, Nk, d, dtype, causal, std_qk)
+SMALL_CASES = [
+    (1, 2, 2, 256, 256, 64, "f32", False, 1.0),     # the tiny fp32 workload at full size
+    (1, 2, 2, 200, 333, 64, "f32", True, 1.0),
+    (2, 3, 3, 300, 300, 128, "bf16", True, 1.0),    # ragged tail in both Q and K tiles
+    (2, 3, 3, 300, 300, 128, "bf16", False, 1.0),
+    (1, 8, 2, 520, 520, 128, "bf16", True, 1.0),    # GQA, causal
+    (2, 4, 4, 333, 333, 64, "bf16", False, 2.0),    # d=64, var-4 scores
+    (1, 4, 1, 257, 257, 64, "bf16", True, 2.0),     # MQA, d=64
+    (1, 2, 2, 200, 200, 256, "bf16", False, 2.0),   # d=256
+    (1, 4, 2, 161, 161, 256, "bf16", True, 1.0),
+    (1, 2, 2, 100, 700, 128, "bf16", False, 1.0),   # Nq < Nk
+    (1, 2, 2, 700, 100, 128, "bf16", False, 1.0),   # Nq > Nk
+    (1, 2, 1, 150, 200, 128, "bf16", True, 1.0),    # causal, Nq != Nk (top-left)
+    (1, 2, 1, 200, 150, 128, "bf16", True, 1.0),
+    (1, 3, 3, 1, 77, 128, "bf16", False, 1.0),      # one query
+    (1, 3, 3, 64, 1, 128, "bf16", False, 1.0),      # one key
+    (1, 2, 2, 129, 129, 128, "bf16", False, 4.0),   # std 4 stress (scores up to ~100)
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SMALL_CASES)),
+                         ids=["B{}H{}kv{}q{}k{}d{}{}{}s{}".format(*c) for c in SMALL_CASES])
+def test_prefill_small(idx):
+    B, Hq, Hkv, Nq, Nk, d, dt, causal, std = SMALL_CASES[idx]
+    check_full(B, Hq, Hkv, Nq, Nk, d, dt, causal, seed=100 + idx, std_qk=std)
+
+
+def test_prefill_single_key_is_exact():
+    # Nk = 1: softmax weight 1, so O equals v_0 bit for bit.
+    q, k, v, o, lse = check_full(2, 4, 2, 70, 1, 128, "bf16", False, seed=3)
+    vv = v[:, 0:1].repeat_interleave(2, dim=2).expand(-1, 70, -1, -1)
+    assert torch.equal(o, vv)
+
+
+def test_prefill_no_keys():
+    dev = torch.device("cuda")
+    q = torch.randn(1, 33, 2, 128, device=dev).to(torch.bfloat16)
+    k = torch.empty(1, 0, 2, 128, device=dev, dtype=torch.bfloat16)
+    o, lse = fa().fa_fwd(q, k, k.clone(), causal=False)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(lse == -math.inf)
+
+
+def test_prefill_zero_query_closed_form():
+    # q = 0: row i averages the visible values; LSE = ln(#visible)
+    dev = torch.device("cuda")
+    _, k, v = SI.prefill_inputs(B=1, Hq=2, Hkv=2, Nq=300, Nk=300, d=128, seed=9, device=dev)
+    q = torch.zeros(1, 300, 2, 128, device=dev, dtype=torch.bfloat16)
+    o, lse = fa().fa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    cnt = np.arange(1, 301)
+    want = np.cumsum(f64(v), axis=1) / cnt[None, :, None, None]
+    assert np.max(np.abs(f64(o) - want)) <= 2e-2
+    assert np.max(np.abs(f64(lse)[0] - np.log(cnt)[None])) <= 1e-3
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    dev = torch.device("cuda")
+    q, k, v = SI.prefill_inputs(B=2, Hq=8, Hkv=2, Nq=190, Nk=190, d=128, seed=21, device=dev)
+    m = fa()
+    for causal in (False, True):
+        o1, l1 = m.fa_fwd(q, k, v, causal=causal)
+        o2, l2 = m.fa_fwd(q, k.repeat_interleave(4, dim=2).contiguous(), v.repeat_interleave(4, dim=2).contiguous(),
+                          causal=causal)
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_deterministic():
+    dev = torch.device("cuda")
+    q, k, v = SI.prefill_inputs(B=2, Hq=4, Hkv=4, Nq=400, Nk=400, d=128, seed=22, device=dev)
+    m = fa()
+    o1, l1 = m.fa_fwd(q, k, v, causal=True)
+    o2, l2 = m.fa_fwd(q, k, v, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_prefill_lse_optional():
+    dev = torch.device("cuda")
+    q, k, v = SI.prefill_inputs(B=1, Hq=2, Hkv=2, Nq=130, Nk=130, d=64, seed=23, device=dev)
+    m = fa()
+    o1, _ = m.fa_fwd(q, k, v, causal=True)
+    o2, l2 = m.fa_fwd(q, k, v, causal=True, want_lse=False)
+    torch.cuda.synchronize()
+    assert l2 is None and torch.equal(o1, o2)
+
+
+# ---------------------------------------------------------------------------
+# full-size workloads, in the launch configuration the benchmark times,
+# checked on sampled rows the oracle computes one by one
+# ---------------------------------------------------------------------------
+def sampled_rows(Nq, rng, n=12):
+    rows = {0, 1, Nq - 1, Nq - 2, Nq // 2}
+    rows.update(rng.integers(0, Nq, n).tolist())
+    return np.array(sorted(rows))
+
+
+@pytest.mark.parametrize("name", list(SI.PREFILL_WORKLOADS))
+def test_prefill_full_size_sampled(name):
+    w = SI.PREFILL_WORKLOADS[name]
+    note(f"full-size prefill {name}")
+    q, k, v, o, lse, scale = run_prefill(w["B"], w["Hq"], w["Hkv"], w["Nq"], w["Nk"], w["d"], w["dtype"],
+                                         w["causal"], w["seed"], w["std_qk"], w["std_v"])
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w["seed"])
+    heads = sorted({0, w["Hq"] - 1, int(rng.integers(0, w["Hq"]))})
+    batches = sorted({0, w["B"] - 1})
+    worst_o = worst_l = 0.0
+    for b in batches:
+        for h in heads:
+            kv = O.kv_head_of(h, w["Hq"], w["Hkv"])
+            rows = sampled_rows(w["Nq"], rng)
+            qs = f64(q[b:b + 1, rows, h:h + 1])
+            ks = f64(k[b:b + 1, :, kv:kv + 1])
+            vs = f64(v[b:b + 1, :, kv:kv + 1])
+            o_ref, l_ref = O.attention_rows(qs, ks, vs, False, scale, 0, 0)
+            if w["causal"]:
+                o_ref = np.zeros_like(o_ref)
+                l_ref = np.zeros_like(l_ref)
+                for n, r in enumerate(rows):
+                    orr, lrr = O.attention_rows(qs[:, n:n + 1], ks[:, :r + 1], vs[:, :r + 1], False, scale, 0, 0)
+                    o_ref[n], l_ref[n] = orr[0], lrr[0]
+            worst_o = max(worst_o, np.max(np.abs(f64(o[b, rows, h]) - o_ref)))
+            worst_l = max(worst_l, np.max(np.abs(f64(lse[b, h, rows]) - l_ref)))
+    note(f"  sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O[w["dtype"]] and worst_l <= TOL_LSE
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+def check_decode(B, Hq, Hkv, cap, d, lens, splits, seed, poison=False):
+    dev = torch.device("cuda")
+    q, kc, vc, _ = SI.decode_inputs(B=B, Hq=Hq, Hkv=Hkv, capacity=cap, d=d, seed=seed, device=dev)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=dev)
+    if poison:
+        SI.poison_cache_tail(kc, vc, lens_t)
+    scale = f32scale(d)
+    o_ref, l_ref = O.decode(f64(q), f64(kc), f64(vc), lens, scale)
+    m = fa()
+    for S in splits:
+        note(f"decode B={B} Hq={Hq} Hkv={Hkv} cap={cap} d={d} S={S} poison={poison}")
+        o, lse = m.fa_fwd_kvcache(q, kc, vc, lens_t, num_splits=S, scale=scale)
+        torch.cuda.synchronize()
+        eo = np.max(np.abs(f64(o)[:, 0] - o_ref))
+        el = np.max(np.abs(np.where(np.isinf(l_ref), 0, f64(lse) - l_ref)))
+        note(f"  max|dO|={eo:.3e} max|dLSE|={el:.3e}")
+        assert eo <= TOL_O["bf16"] and el <= TOL_LSE
+        assert np.array_equal(np.isinf(f64(lse)), np.isinf(l_ref))
+
+
+def test_decode_small_splits():
+    check_decode(5, 8, 2, 300, 128, [300, 1, 64, 65, 200], [1, 2, 3, 5, 8], seed=31)
+
+
+def test_decode_group_and_dims():
+    check_decode(3, 16, 1, 257, 128, [257, 100, 3], [1, 4], seed=32)   # 16 query heads per KV head
+    check_decode(3, 4, 4, 200, 64, [200, 130, 1], [1, 2], seed=33)
+    check_decode(2, 8, 2, 190, 256, [190, 67], [1, 3], seed=34)
+
+
+def test_decode_empty_sequence():
+    # L_b = 0: O = 0, LSE = -inf, for any split count
+    dev = torch.device("cuda")
+    q, kc, vc, _ = SI.decode_inputs(B=3, Hq=4, Hkv=2, capacity=128, d=128, seed=35, device=dev)
+    lens = torch.tensor([0, 128, 0], dtype=torch.int32, device=dev)
+    for S in (1, 2, 4):
+        o, lse = fa().fa_fwd_kvcache(q, kc, vc, lens, num_splits=S)
+        torch.cuda.synchronize()
+        assert torch.all(o[0] == 0) and torch.all(o[2] == 0)
+        assert torch.all(lse[0] == -math.inf) and torch.all(lse[2] == -math.inf)
+        assert torch.isfinite(lse[1]).all()
+
+
+def test_decode_never_reads_past_length():
+    # K rows beyond L_b are 1e4 (would dominate the softmax), V rows are NaN
+    check_decode(4, 8, 2, 320, 128, [1, 77, 256, 319], [1, 2, 5], seed=36, poison=True)
+
+
+def test_decode_equals_prefill_on_prefix():
+    dev = torch.device("cuda")
+    q, kc, vc, _ = SI.decode_inputs(B=2, Hq=8, Hkv=2, capacity=256, d=128, seed=37, device=dev)
+    lens = [256, 256]
+    lt = torch.tensor(lens, dtype=torch.int32, device=dev)
+    m = fa()
+    od, ld = m.fa_fwd_kvcache(q, kc, vc, lt, num_splits=1)
+    op, lp = m.fa_fwd(q, kc, vc, causal=False)
+    torch.cuda.synchronize()
+    assert (od.float() - op.float()).abs().max().item() <= 2e-2
+    assert (ld - lp[:, :, 0]).abs().max().item() <= 1e-3
+
+
+@pytest.mark.parametrize("name", list(SI.DECODE_WORKLOADS))
+def test_decode_full_size_sampled(name):
+    w = SI.DECODE_WORKLOADS[name]
+    dev = torch.device("cuda")
+    note(f"full-size decode {name}")
+    q, kc, vc, lens = SI.decode_inputs(device=dev, **w)
+    scale = f32scale(w["d"])
+    m = fa()
+    S = m.fa_kvcache_default_splits(w["B"], w["Hkv"], w["capacity"])
+    o, lse = m.fa_fwd_kvcache(q, kc, vc, lens, num_splits=S, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+    rng = np.random.default_rng(w["seed"])
+    lens_h = lens.cpu().numpy()
+    worst_o = worst_l = 0.0
+    for b in sorted({0, w["B"] - 1, *rng.integers(0, w["B"], 4).tolist()}):
+        n = int(lens_h[b])
+        heads = sorted({0, w["Hq"] - 1, int(rng.integers(0, w["Hq"]))})
+        o_ref, l_ref = O.decode(f64(q[b:b + 1]), f64(kc[b:b + 1, :n]), f64(vc[b:b + 1, :n]), [n], scale, heads)
+        for h in heads:
+            worst_o = max(worst_o, np.max(np.abs(f64(o[b, 0, h]) - o_ref[0, h])))
+            worst_l = max(worst_l, abs(float(lse[b, h]) - l_ref[0, h]))
+    note(f"  S={S} sampled max|dO|={worst_o:.3e} max|dLSE|={worst_l:.3e}")
+    assert worst_o <= TOL_O["bf16"] and worst_l <= TOL_LSE
