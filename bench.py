@@ -1,0 +1,222 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+fa_fwd on the training-shape causal workload (B=8, H=16, N=2048, d=128,
+bf16) followed by fa_fwd_kvcache (split-KV decode + combine) on the GQA
+decode workload (B=64, Hq=32, Hkv=8, d=128, cache capacity 8192, lengths
+uniform in [1024, 8192]). Inputs are generated on the device before the
+timed region. Each launch is bracketed by HIP events on the stream it runs
+on; `value` is the prefill's algorithmic TFLOP/s (4*B*H*Nq*Nk*d, halved for
+causal) over its mean event time, and the decode's algorithmic GB/s is
+reported beside it. Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill NAME]
+                    [--no-cpu-baseline] [--splits S]
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
+PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+PEAK_HBM_GBS = 8000.0
+DEFAULT_PREFILL = "mha_bf16_causal_b8_h16_n2048_d128"
+DEFAULT_DECODE = "gqa_bf16_decode_b64_h32kv8_cap8192_d128"
+PREFILL_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_online_amd", "csrc", "fa_fwd_bf16.hip")
+DECODE_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_online_amd", "csrc", "fa_decode.hip")
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def prefill_flops(w):
+    f = 4.0 * w["B"] * w["Hq"] * w["Nq"] * w["Nk"] * w["d"]
+    return f / 2 if w["causal"] else f
+
+
+def stored_traffic(kernel_key, src):
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(kernel_key)
+    if not rec or rec.get("source_sha256_16") != source_hash(src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(name, w, budget_s=12.0):
+    """The CPU float64 oracle, as is, on whole (batch, head) slices of the
+    same prefill workload until about `budget_s` seconds have passed."""
+    import numpy as np
+    import torch
+
+    import seeded_inputs as SI
+    from oracle import sdpa as O
+
+    q, k, v = SI.prefill_inputs(device="cpu", **w)
+    f64 = lambda t: t.to(torch.float64).numpy()
+    scale = float(np.float32(1.0 / math.sqrt(w["d"])))
+    G = w["Hq"] // w["Hkv"]
+    done = 0
+    t0 = time.perf_counter()
+    for b in range(w["B"]):
+        for h in range(w["Hq"]):
+            kv = h // G
+            O.attention_rows(f64(q[b:b + 1, :, h:h + 1]), f64(k[b:b + 1, :, kv:kv + 1]),
+                             f64(v[b:b + 1, :, kv:kv + 1]), w["causal"], scale, 0, 0)
+            done += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    per_head = prefill_flops(dict(w, B=1, Hq=1))
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    return {"value": per_head * done / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{done} of {w['B'] * w['Hq']} (batch, head) slices of {name}, "
+                      f"full fp64 score matrix each, {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--prefill", default=DEFAULT_PREFILL)
+    ap.add_argument("--decode", default=DEFAULT_DECODE)
+    ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on a single GPU's share; no multi-GPU path is built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_online_amd as fa
+    import seeded_inputs as SI
+
+    fa.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    wp = SI.PREFILL_WORKLOADS[args.prefill]
+    wd = SI.DECODE_WORKLOADS[args.decode]
+    q, k, v = SI.prefill_inputs(device=dev, **wp)
+    scale_p = 1.0 / math.sqrt(wp["d"])
+    o = torch.empty_like(q)
+    lse = torch.empty((wp["B"], wp["Hq"], wp["Nq"]), dtype=torch.float32, device=dev)
+
+    qd, kc, vc, lens = SI.decode_inputs(device=dev, **wd)
+    S = args.splits or fa.fa_kvcache_default_splits(wd["B"], wd["Hkv"], wd["capacity"])
+    od = torch.empty_like(qd)
+    lsed = torch.empty((wd["B"], wd["Hq"]), dtype=torch.float32, device=dev)
+    ws_bytes = fa.fa_fwd_kvcache_workspace_size(wd["B"], wd["Hq"], wd["d"], S)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    scale_d = 1.0 / math.sqrt(wd["d"])
+    lens_sum = int(lens.to(torch.int64).sum().item())
+    dec_bytes = (lens_sum * wd["Hkv"] * wd["d"] * 2 * 2            # K and V rows actually visible
+                 + qd.numel() * 2 + od.numel() * 2 + lsed.numel() * 4 + lens.numel() * 4)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=wp["causal"], scale=scale_p)
+        if ev is not None:
+            ev[1].record()
+        fa.fa_fwd_kvcache(qd, kc, vc, lens, o=od, lse=lsed, num_splits=S, scale=scale_d, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    pf_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dc_ms = [e[1].elapsed_time(e[2]) for e in events]
+    pf_mean = sum(pf_ms) / len(pf_ms)
+    dc_mean = sum(dc_ms) / len(dc_ms)
+    flops = prefill_flops(wp)
+    tflops = flops / (pf_mean * 1e-3) / 1e12
+    gbs = dec_bytes / (dc_mean * 1e-3) / 1e9
+
+    traffic = stored_traffic("prefill:" + args.prefill, PREFILL_KERNEL_SOURCE)
+    dec_traffic = stored_traffic("decode:" + args.decode, DECODE_KERNEL_SOURCE)
+
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": args.prefill,
+            "batch": wp["B"], "q_heads": wp["Hq"], "kv_heads": wp["Hkv"], "seq_len": wp["Nq"],
+            "head_dim": wp["d"], "causal": wp["causal"],
+            "decode_workload": args.decode, "decode_num_splits": S,
+        },
+        "roofline": {
+            "kernel": f"fwd_bf16_kernel<{wp['d']}>",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+            "algorithmic_flops_per_launch": flops,
+            "mean_launch_ms": round(pf_mean, 5),
+        },
+        "decode": {
+            "value": round(gbs, 1),
+            "unit": "GB/s",
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
+                         "algorithmic_bytes_per_launch": dec_bytes, "mean_launch_ms": round(dc_mean, 5)},
+            "num_splits": S,
+        },
+        "device": {"name": props.name, "cus": props.multi_processor_count,
+                   "arch": getattr(props, "gcnArchName", "")},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.prefill, wp, args.cpu_budget)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

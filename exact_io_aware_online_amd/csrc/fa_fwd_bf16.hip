@@ -1,38 +1,49 @@
 // fa_fwd_bf16.hip - prefill / training forward in bf16 for gfx950.
 //
 // One workgroup owns one tile of BM query rows of one (batch, query head)
-// and streams every key/value tile it may see (FlashAttention: Part 2,
-// section 1.2: query-row tiles are independent units of work; section 1.3:
-// each wavefront owns whole rows so no partial results cross wavefronts).
-// Per key tile (FlashAttention: Part 2, section 6.2): score tile ->
-// online softmax -> value accumulation -> discard; the N x N matrix never
-// leaves registers.
+// and streams every key/value tile those rows may see (FlashAttention:
+// Part 2, section 1.2: query-row tiles are independent units of work;
+// section 1.3: each wavefront owns whole rows, so no partial results cross
+// wavefronts). Per key tile (FlashAttention: Part 2, section 6.2): score
+// tile -> online softmax -> value accumulation -> discard; the N x N matrix
+// never leaves registers.
 //
-// The score tile is computed transposed, S^T = K Q^T, with the 32x32x16
-// bf16 MFMA: its accumulator puts one query per lane (lane % 32), so each
-// lane's running max, running sum and output column belong to a single
-// query and the row reductions are in-lane plus one exchange with the lane
-// 32 away. The probabilities P^T then feed O^T += V^T P^T directly as the
-// B operand, with no trip through LDS. K tiles sit in LDS row-major; V tiles
-// are written to LDS transposed (dimension-major) with the key order
-// permuted to match where the accumulator left each probability.
+// Data movement. K and V tiles go HBM -> LDS with direct-to-LDS 16-byte
+// loads (global_load_lds_dwordx4) into an NST-stage ring, so a tile is in
+// flight while earlier ones are consumed and no registers stage it. The
+// loads are issued from inline assembly: the compiler does not track them,
+// and the pipeline's own waits (vmcnt) and one s_barrier per tile order
+// them. Inside a stage each row's 16-byte chunks are XOR-swizzled so the
+// MFMA operand reads below hit distinct LDS banks.
 //
-// Softmax runs in base 2: t = s * scale * log2(e), running maximum m in the
-// same units, alpha = 2^(m - m') (FlashAttention: Part 2, section 6.2 gives
-// alpha = e^(m - m'); the two agree because e^x = 2^(x log2 e)).
-// Normalisation is deferred to the end (FlashAttention: Part 2, section
-// 1.3), where the row's log-sum-exp is written as ln2 * (m + log2 l).
+// Math. The score tile is computed transposed, S^T = K Q^T, on the
+// 32x32x16 bf16 MFMA: its accumulator gives each lane (lane % 32) a single
+// query, so the running max, the running sum and the output column of that
+// query live in that lane and the row max needs one exchange with the lane
+// 32 away. P^T then feeds O^T += V^T P^T directly as the B operand. The
+// V^T A operand is read from the row-major V tile with ds_read_b64_tr_b16,
+// which transposes 16-bit elements across each group of 16 lanes.
+//
+// Softmax runs in base 2: t = s * scale * log2(e), the running maximum m in
+// the same units, alpha = 2^(m - m') (FlashAttention: Part 2, section 6.2
+// gives alpha = e^(m - m'); e^x = 2^(x log2 e)). When no row maximum of a
+// wavefront moved, alpha is exactly 1 for every row and the rescale of the
+// accumulator is skipped (bit-identical). Normalisation is deferred to the
+// end (FlashAttention: Part 2, section 1.3), where the row's log-sum-exp is
+// written as ln2 * (m + log2 l).
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
+#define LDS3 __attribute__((address_space(3)))
+
 struct FwdParams {
-  const bf16* __restrict__ q;
-  const bf16* __restrict__ k;
-  const bf16* __restrict__ v;
-  bf16* __restrict__ o;
+  const char* __restrict__ q;
+  const char* __restrict__ k;
+  const char* __restrict__ v;
+  char* __restrict__ o;
   float* __restrict__ lse;
   int Nq, Nk, Hq, Hkv, group;
   int causal;
@@ -40,261 +51,311 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-template <int D, int BN, int NW>
-struct Tile {
-  static constexpr int BM = NW * 32;          // query rows per workgroup
+template <int D_, int BN_, int NW_, int QB_, int NST_>
+struct Cfg {
+  static constexpr int D = D_, BN = BN_, NW = NW_, QB = QB_, NST = NST_;
+  static constexpr int BM = NW * 32 * QB;          // query rows per workgroup
   static constexpr int THREADS = NW * 64;
-  static constexpr int KS = D + 8;            // K row stride in LDS (bf16), padded
-  static constexpr int VS = BN + 8;           // V^T row stride in LDS (bf16), padded
-  static constexpr int LDS_K = BN * KS;
-  static constexpr int LDS_V = D * VS;
-  static constexpr int K_CHUNKS = BN * D / 8;             // 16-byte pieces of a K tile
-  static constexpr int K_ITERS = (K_CHUNKS + THREADS - 1) / THREADS;
-  static constexpr int V_UNITS = (BN / 4) * (D / 8);      // 4 keys x 8 dims each
-  static constexpr int V_ITERS = (V_UNITS + THREADS - 1) / THREADS;
-  static_assert(BN % 32 == 0, "key tile must be a multiple of 32");
-  static_assert(D % 32 == 0, "head dim must be a multiple of 32");
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int DMA = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per tile
+  static_assert(DMA >= 1 && TILE_BYTES % (THREADS * 16) == 0, "tile does not split over the threads");
+  static_assert(BN % 32 == 0 && D % 32 == 0, "tile shapes");
+  static_assert(NST >= 2 && (NST - 2) * 2 * DMA <= 63, "vmcnt range");
 };
 
-// Slot of the first of four consecutive keys (4*kg .. 4*kg+3, kg < 4) of a
-// 16-key block inside the transposed V tile. The S^T accumulator leaves key
-// 8*(i/4) + 4*g + (i%4) of each 16-key half in register i of lane half g;
-// storing that key at slot 8*g + i makes every lane's eight B-operand keys
-// contiguous in LDS.
-__device__ __forceinline__ int vt_slot(int kg) { return ((kg & 1) << 3) | ((kg >> 1) << 2); }
+// Chunk swizzle of a tile row: physical chunk = logical chunk ^ swz(row).
+// For rows of 16+ chunks the swizzle depends on row % 16 and spreads the
+// 16 consecutive rows a b128 read touches over 16 chunks; pairs of
+// consecutive rows (4 rows per transposed read) land on disjoint chunk pairs.
+// Rows of 8 chunks (d = 64) are 128 bytes, two per 256-byte bank line, so
+// the swizzle follows row / 2 and the row parity supplies the other half.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CPR >= 16) {
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 3) << 1) | ((x >> 2) & 1);
+  }
+}
 
-template <int D, int BN, int NW>
-__global__ __launch_bounds__(NW * 64) void fwd_bf16_kernel(FwdParams p) {
-  using T = Tile<D, BN, NW>;
-  __shared__ __attribute__((aligned(16))) bf16 smem[T::LDS_K + T::LDS_V];
-  bf16* Ks = smem;
-  bf16* Vt = smem + T::LDS_K;
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at
+// lds_addr + 16 l (lds_addr wave-uniform, in M0).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 i16x4*)(uintptr_t)lds_addr);
+}
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
+  constexpr int D = C::D, BN = C::BN, QB = C::QB, NST = C::NST, CPR = C::CPR;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 5;   // which half of the wavefront
-  const int r32 = lane & 31; // query within the wavefront's 32 rows
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
+  const int g = lane >> 5;    // half of the wavefront
+  const int r32 = lane & 31;  // query (S^T column) within a 32-row block
 
   int qt = blockIdx.x;
   if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
   const int hq = blockIdx.y;
   const int b = blockIdx.z;
   const int kvh = hq / p.group;
-  const int q0 = qt * T::BM;
-  const int qw0 = q0 + wave * 32;
-  const int my_q = qw0 + r32;
+  const int q0 = qt * C::BM;
+  const int qw0 = q0 + wave * 32 * QB;  // first query row of this wavefront
 
-  const int64_t q_stride = (int64_t)p.Hq * D;   // elements between query rows
-  const int64_t kv_stride = (int64_t)p.Hkv * D; // elements between key rows
+  const int64_t q_row = (int64_t)p.Hq * D * 2;    // bytes between query rows
+  const int kv_row = p.Hkv * D * 2;                // bytes between key rows
 
-  // Q^T as the B operand: register i of k-step ks holds Q[my_q][16 ks + 8 g + i].
-  bf16x8 qf[D / 16];
-  {
-    const bf16* qrow = p.q + ((int64_t)b * p.Nq + my_q) * q_stride + (int64_t)hq * D;
+  int kend = p.Nk;
+  if (p.causal) kend = min(kend, q0 + C::BM);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  // ---- DMA addressing: load j of a tile fills slot j*THREADS + tid
+  const char* kbase = p.k + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  const char* vbase = p.v + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  int dma_row[C::DMA], dma_col[C::DMA];
+#pragma unroll
+  for (int j = 0; j < C::DMA; ++j) {
+    const int slot = j * C::THREADS + tid;
+    const int row = slot / CPR;
+    dma_row[j] = row;
+    dma_col[j] = ((slot % CPR) ^ swz<CPR>(row)) * 16;
+  }
+  const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
+
+  auto issue_tile = [&](int t) {
+    const int j0 = t * BN;
+    const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
+    const char* ks = kbase + (int64_t)j0 * kv_row;
+    const char* vs = vbase + (int64_t)j0 * kv_row;
+    const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::STAGE_BYTES);
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) {
+      const uint32_t off = (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]);
+      dma16(ks, off, st + j * C::THREADS * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < C::DMA; ++j) {
+      const uint32_t off = (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]);
+      dma16(vs, off, st + C::TILE_BYTES + j * C::THREADS * 16);
+    }
+  };
+
+  // start the pipeline before loading Q
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < ntiles) issue_tile(s);
+
+  // ---- Q^T as B operand: register i of k-step ks = Q[row][16 ks + 8 g + i]
+  bf16x8 qf[QB][D / 16];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int row = qw0 + qb * 32 + r32;
+    const char* qrow = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      if (my_q < p.Nq) {
-        qf[ks] = *reinterpret_cast<const bf16x8*>(qrow + ks * 16 + g * 8);
-      } else {
-        qf[ks] = bf16x8{};
-      }
+      qf[qb][ks] = row < p.Nq ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
 
-  int kend = p.Nk;
-  if (p.causal) kend = min(kend, q0 + T::BM);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  f32x16 acc[QB][D / 32];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[qb][dt] = f32x16{};
+  float m[QB], l[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m[qb] = -INFINITY;  // running max of t, base-2 units
+    l[qb] = 0.f;        // running sum of 2^(t - m) over this lane's keys
+  }
 
-  f32x16 acc[D / 32];
+  // ---- per-lane LDS read offsets
+  // K (b128): row = 32 nb + r32, logical chunk 2 ks + g
+  const int ksw = swz<CPR>(r32);
+  const uint32_t k_rd = (uint32_t)(r32 * D * 2);
+  // V (transposed b64): 16-lane group grp = lane / 16 reads rows
+  // 16 kk + 8 h + 4 g + (lane % 16) / 4 at columns 32 dt + 16 (grp % 2) + 4 (lane % 4)
+  const int vi = lane & 15;
+  const int vgrp = lane >> 4;
+  uint32_t v_rd[2];
+  int vsw[2];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
-  float m = -INFINITY;  // running max of t, base-2 units
-  float l = 0.f;        // running sum of 2^(t - m) over this lane's keys
+  for (int h = 0; h < 2; ++h) {
+    const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
+    vsw[h] = swz<CPR>(row);
+    v_rd[h] = (uint32_t)(row * D * 2 + (vi & 1) * 8);
+  }
+  const int vcol = (vgrp & 1) * 2 + ((vi & 3) >> 1);  // logical chunk within a 32-column block
 
-  const bf16* kbase = p.k + (int64_t)b * p.Nk * kv_stride + (int64_t)kvh * D;
-  const bf16* vbase = p.v + (int64_t)b * p.Nk * kv_stride + (int64_t)kvh * D;
-
-  u32x4 kreg[T::K_ITERS];
-  u32x4 vreg[T::V_ITERS][4];
-
-  auto load_tile = [&](int j0) {
-#pragma unroll
-    for (int it = 0; it < T::K_ITERS; ++it) {
-      const int c = tid + it * T::THREADS;
-      const int row = c / (D / 8), col = c % (D / 8);
-      const int key = j0 + row;
-      if (c < T::K_CHUNKS && key < p.Nk) {
-        kreg[it] = load_u32x4(kbase + (int64_t)key * kv_stride + col * 8);
-      } else {
-        kreg[it] = u32x4{0, 0, 0, 0};
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < T::V_ITERS; ++it) {
-      const int u = tid + it * T::THREADS;
-      const int kg = u % (BN / 4), dc = u / (BN / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + kg * 4 + r;
-        if (u < T::V_UNITS && key < p.Nk) {
-          vreg[it][r] = load_u32x4(vbase + (int64_t)key * kv_stride + dc * 8);
-        } else {
-          vreg[it][r] = u32x4{0, 0, 0, 0};
-        }
-      }
-    }
-  };
-
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int it = 0; it < T::K_ITERS; ++it) {
-      const int c = tid + it * T::THREADS;
-      if (c < T::K_CHUNKS) {
-        const int row = c / (D / 8), col = c % (D / 8);
-        store_u32x4(Ks + row * T::KS + col * 8, kreg[it]);
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < T::V_ITERS; ++it) {
-      const int u = tid + it * T::THREADS;
-      if (u < T::V_UNITS) {
-        const int kg = u % (BN / 4), dc = u / (BN / 4);
-        const int slot = (kg >> 2) * 16 + vt_slot(kg & 3);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int w = j >> 1;
-          uint32_t lo, hi;
-          if (j & 1) {
-            lo = (vreg[it][0][w] >> 16) | (vreg[it][1][w] & 0xffff0000u);
-            hi = (vreg[it][2][w] >> 16) | (vreg[it][3][w] & 0xffff0000u);
-          } else {
-            lo = (vreg[it][0][w] & 0xffffu) | (vreg[it][1][w] << 16);
-            hi = (vreg[it][2][w] & 0xffffu) | (vreg[it][3][w] << 16);
-          }
-          *reinterpret_cast<u32x2*>(Vt + (dc * 8 + j) * T::VS + slot) = u32x2{lo, hi};
-        }
-      }
-    }
-  };
-
-  if (ntiles > 0) load_tile(0);
   for (int t = 0; t < ntiles; ++t) {
-    const int j0 = t * BN;
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();  // the tile is in LDS
-    if (t + 1 < ntiles) load_tile(j0 + BN);  // in flight during the math below
-
-    // keys of this tile all lie beyond every query of this wavefront
-    if (p.causal && j0 > qw0 + 31) continue;
-    const bool need_mask = (j0 + BN > p.Nk) || (p.causal && j0 + BN - 1 > qw0);
-
-    // S^T = K Q^T for BN keys x 32 queries
-    f32x16 s[BN / 32];
-#pragma unroll
-    for (int nb = 0; nb < BN / 32; ++nb) {
-      s[nb] = f32x16{};
-      const bf16* krow = Ks + (nb * 32 + r32) * T::KS + g * 8;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks * 16);
-        s[nb] = mfma32x32x16(kf, qf[ks], s[nb]);
-      }
+    // own loads of tile t are done when at most the later tiles' remain
+    if constexpr (NST == 3) {
+      if (t + 1 < ntiles) wait_vmcnt<2 * C::DMA>(); else wait_vmcnt<0>();
+    } else {
+      wait_vmcnt<0>();
     }
+    barrier();  // everyone's loads of tile t landed; tile t-1 is no longer read
+    if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
 
-    if (need_mask) {
+    const int j0 = t * BN;
+    if (p.causal && j0 > qw0 + 32 * QB - 1) continue;  // every key is in this wavefront's future
+    const bool need_mask = (j0 + BN > p.Nk) || (p.causal && j0 + BN - 1 > qw0);
+    const uint32_t kst = lds0 + (uint32_t)((t % NST) * C::STAGE_BYTES);
+    const uint32_t vst = kst + C::TILE_BYTES;
+
+    // S^T = K Q^T: BN keys x 32 queries per query block
+    f32x16 s[QB][BN / 32];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int nb = 0; nb < BN / 32; ++nb) s[qb][nb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < BN / 32; ++nb) {
+        const uint32_t a = kst + k_rd + nb * 32 * D * 2 + (((2 * ks + g) ^ ksw) * 16);
+        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)a;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s[qb][nb] = mfma32x32x16(kf, qf[qb][ks], s[qb][nb]);
+      }
+    }
+
+    bool moved = false;
+    float alpha[QB];
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (need_mask) {
+        // key j0 + 4g + off (off = 32 nb + 8 (i/4) + i%4) is visible iff off <= lim
+        const int my_q = qw0 + qb * 32 + r32;
+        const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - j0 - 4 * g;
+#pragma unroll
+        for (int nb = 0; nb < BN / 32; ++nb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int off = nb * 32 + 8 * (i >> 2) + (i & 3);
+            if (off > lim) s[qb][nb][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int nb = 0; nb < BN / 32; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][nb][i]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m[qb], mx * p.c);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // never (-inf) - (-inf)
+      moved |= m_new != m[qb];
+      alpha[qb] = exp2_fast(m[qb] - m_use);
+      m[qb] = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < BN / 32; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = j0 + nb * 32 + 8 * (i >> 2) + 4 * g + (i & 3);
-          if (key >= p.Nk || (p.causal && key > my_q)) s[nb][i] = -INFINITY;
+          const float pv = exp2_fast(fmaf(s[qb][nb][i], p.c, -m_use));
+          s[qb][nb][i] = pv;
+          rs += pv;
         }
-      }
+      l[qb] = fmaf(l[qb], alpha[qb], rs);
     }
 
-    float mx = -INFINITY;
+    // P^T as B operands: 16-key step kk takes registers 8 (kk % 2) .. +7 of
+    // accumulator kk / 2 (keys 8 (i / 4) + 4 g + i % 4 of that half).
+    bf16x8 pf[QB][BN / 16];
 #pragma unroll
-    for (int nb = 0; nb < BN / 32; ++nb)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nb][i]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m, mx * p.c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // no (-inf) - (-inf)
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
-
-    float rs = 0.f;
+      for (int kk = 0; kk < BN / 16; ++kk) {
+        const int nb = kk >> 1, h = (kk & 1) * 8;
+        u32x4 w;
 #pragma unroll
-    for (int nb = 0; nb < BN / 32; ++nb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = exp2_fast(fmaf(s[nb][i], p.c, -m_use));
-        s[nb][i] = pv;
-        rs += pv;
+        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][nb][h + 2 * e], s[qb][nb][h + 2 * e + 1]);
+        pf[qb][kk] = __builtin_bit_cast(bf16x8, w);
       }
-    l = fmaf(l, alpha, rs);
 
-    // P^T as B operands: 16-key step kk takes registers 8*(kk%2) .. +7 of
-    // accumulator kk/2 (keys 8*(i/4) + 4g + i%4 of that 16-key half).
-    bf16x8 pf[BN / 16];
+    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // wave-uniform: some row max moved
 #pragma unroll
-    for (int kk = 0; kk < BN / 16; ++kk) {
-      const int nb = kk >> 1, h = (kk & 1) * 8;
-      u32x4 w;
+      for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[nb][h + 2 * e], s[nb][h + 2 * e + 1]);
-      pf[kk] = __builtin_bit_cast(bf16x8, w);
+        for (int dt = 0; dt < D / 32; ++dt) acc[qb][dt] *= alpha[qb];
     }
-
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
 
     // O^T += V^T P^T
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const bf16* vrow = Vt + (dt * 32 + r32) * T::VS + g * 8;
 #pragma unroll
       for (int kk = 0; kk < BN / 16; ++kk) {
-        const bf16x8 vf = *reinterpret_cast<const bf16x8*>(vrow + kk * 16);
-        acc[dt] = mfma32x32x16(vf, pf[kk], acc[dt]);
+        i16x4 v0, v1;
+        {
+          const uint32_t c0 = (uint32_t)(((4 * dt + vcol) ^ vsw[0]) * 16);
+          const uint32_t c1 = (uint32_t)(((4 * dt + vcol) ^ vsw[1]) * 16);
+          v0 = ds_read_tr(vst + kk * 16 * D * 2 + v_rd[0] + c0);
+          v1 = ds_read_tr(vst + kk * 16 * D * 2 + v_rd[1] + c1);
+        }
+        // registers 0..3: keys 4 g + r; 4..7: keys 8 + 4 g + r (of block kk)
+        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma32x32x16(va, pf[qb][kk], acc[qb][dt]);
       }
     }
   }
 
-  // Epilogue: combine the two lane halves' partial sums, normalise once.
-  const float lt = l + swap_halves(l);
-  const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  if (my_q < p.Nq) {
-    bf16* orow = p.o + ((int64_t)b * p.Nq + my_q) * q_stride + (int64_t)hq * D;
+  // ---- epilogue: combine the two lane halves' sums, normalise once
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+  for (int qb = 0; qb < QB; ++qb) {
+    const int my_q = qw0 + qb * 32 + r32;
+    const float lt = l[qb] + swap_halves(l[qb]);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (my_q < p.Nq) {
+      char* orow = p.o + ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = dt * 32 + 8 * j + 4 * g;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[dt][4 * j + 0] * inv, acc[dt][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + d0) = w;
+      for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = dt * 32 + 8 * j + 4 * g;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
+          w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0 * 2) = w;
+        }
       }
-    }
-    if (p.lse != nullptr && g == 0) {
-      p.lse[((int64_t)b * p.Hq + hq) * p.Nq + my_q] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
+      if (p.lse != nullptr && g == 0) {
+        p.lse[((int64_t)b * p.Hq + hq) * p.Nq + my_q] =
+            lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
+      }
     }
   }
 }
 
-template <int D, int BN, int NW>
+template <class C>
 hipError_t launch(const FwdArgs& a, hipStream_t stream) {
-  using T = Tile<D, BN, NW>;
   FwdParams p;
-  p.q = static_cast<const bf16*>(a.q);
-  p.k = static_cast<const bf16*>(a.k);
-  p.v = static_cast<const bf16*>(a.v);
-  p.o = static_cast<bf16*>(a.o);
+  p.q = static_cast<const char*>(a.q);
+  p.k = static_cast<const char*>(a.k);
+  p.v = static_cast<const char*>(a.v);
+  p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
   p.Nq = a.Nq;
   p.Nk = a.Nk;
@@ -302,10 +363,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.group = a.Hq / a.Hkv;
   p.causal = a.causal;
-  p.n_qtiles = (a.Nq + T::BM - 1) / T::BM;
+  p.n_qtiles = (a.Nq + C::BM - 1) / C::BM;
   p.c = a.scale * kLog2e;
   dim3 grid(p.n_qtiles, a.Hq, a.B);
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BN, NW>), grid, dim3(T::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((fwd_bf16_kernel<C>), grid, dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -315,9 +376,9 @@ bool fwd_bf16_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
-    case 64: return launch<64, 64, 4>(a, stream);
-    case 128: return launch<128, 64, 4>(a, stream);
-    case 256: return launch<256, 32, 4>(a, stream);
+    case 64: return launch<Cfg<64, 64, 8, 1, 3>>(a, stream);
+    case 128: return launch<Cfg<128, 64, 8, 1, 3>>(a, stream);
+    case 256: return launch<Cfg<256, 32, 4, 1, 3>>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
