@@ -31,6 +31,10 @@
 // accumulator is skipped (bit-identical). Normalisation is deferred to the
 // end (FlashAttention: Part 2, section 1.3), where the row's log-sum-exp is
 // written as ln2 * (m + log2 l).
+#include <stdlib.h>
+
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -51,9 +55,10 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-template <int D_, int BN_, int NW_, int QB_, int NST_>
+template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_, QB = QB_, NST = NST_;
+  static constexpr int WAVES_PER_SIMD = WPS_;  // register budget: 512 / WPS per lane
   static constexpr int BM = NW * 32 * QB;          // query rows per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -88,6 +93,10 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
 }
 
+// Growth of a row maximum (base-2 units) tolerated before the running
+// maximum and the accumulator are rescaled.
+constexpr float kSlack = 8.f;
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
@@ -104,7 +113,7 @@ __device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
 }
 
 template <class C>
-__global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel(FwdParams p) {
   constexpr int D = C::D, BN = C::BN, QB = C::QB, NST = C::NST, CPR = C::CPR;
   __shared__ __attribute__((aligned(1024))) char smem[NST * C::STAGE_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
@@ -190,25 +199,37 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
     l[qb] = 0.f;        // running sum of 2^(t - m) over this lane's keys
   }
 
-  // ---- per-lane LDS read offsets
+  // ---- per-lane LDS read offsets within a stage (the parts that vary by
+  // 32-key block nb or 16-key block kk are compile-time immediates)
   // K (b128): row = 32 nb + r32, logical chunk 2 ks + g
-  const int ksw = swz<CPR>(r32);
-  const uint32_t k_rd = (uint32_t)(r32 * D * 2);
+  uint32_t k_off[D / 16];
+  {
+    const int ksw = swz<CPR>(r32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
+  }
   // V (transposed b64): 16-lane group grp = lane / 16 reads rows
   // 16 kk + 8 h + 4 g + (lane % 16) / 4 at columns 32 dt + 16 (grp % 2) + 4 (lane % 4)
-  const int vi = lane & 15;
-  const int vgrp = lane >> 4;
-  uint32_t v_rd[2];
-  int vsw[2];
+  uint32_t v_off[D / 32][2];
+  {
+    const int vi = lane & 15;
+    const int vgrp = lane >> 4;
+    const int vcol = (vgrp & 1) * 2 + ((vi & 3) >> 1);  // logical chunk within a 32-column block
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
-    vsw[h] = swz<CPR>(row);
-    v_rd[h] = (uint32_t)(row * D * 2 + (vi & 1) * 8);
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
+      const int sw = swz<CPR>(row);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        v_off[dt][h] = (uint32_t)(C::TILE_BYTES + row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
+    }
   }
-  const int vcol = (vgrp & 1) * 2 + ((vi & 3) >> 1);  // logical chunk within a 32-column block
 
-  for (int t = 0; t < ntiles; ++t) {
+  // Every wavefront takes part in every tile's wait + barrier + prefetch,
+  // in order; it computes on tiles [0, nt_w), of which the first nt_full
+  // need no mask. Peeling the loop this way keeps the accumulator's
+  // loop-carried registers free of branches.
+  auto sync_tile = [&](int t) {
     // own loads of tile t are done when at most the later tiles' remain
     if constexpr (NST == 3) {
       if (t + 1 < ntiles) wait_vmcnt<2 * C::DMA>(); else wait_vmcnt<0>();
@@ -217,12 +238,12 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
     }
     barrier();  // everyone's loads of tile t landed; tile t-1 is no longer read
     if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
+  };
 
+  auto compute_tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int j0 = t * BN;
-    if (p.causal && j0 > qw0 + 32 * QB - 1) continue;  // every key is in this wavefront's future
-    const bool need_mask = (j0 + BN > p.Nk) || (p.causal && j0 + BN - 1 > qw0);
-    const uint32_t kst = lds0 + (uint32_t)((t % NST) * C::STAGE_BYTES);
-    const uint32_t vst = kst + C::TILE_BYTES;
+    const uint32_t stg = lds0 + (uint32_t)((t % NST) * C::STAGE_BYTES);
 
     // S^T = K Q^T: BN keys x 32 queries per query block
     f32x16 s[QB][BN / 32];
@@ -234,18 +255,17 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
       for (int nb = 0; nb < BN / 32; ++nb) {
-        const uint32_t a = kst + k_rd + nb * 32 * D * 2 + (((2 * ks + g) ^ ksw) * 16);
-        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)a;
+        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)(stg + k_off[ks] + nb * 32 * D * 2);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) s[qb][nb] = mfma32x32x16(kf, qf[qb][ks], s[qb][nb]);
       }
     }
 
     bool moved = false;
-    float alpha[QB];
+    float alpha[QB], m_cand[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
-      if (need_mask) {
+      if constexpr (MASK) {
         // key j0 + 4g + off (off = 32 nb + 8 (i/4) + i%4) is visible iff off <= lim
         const int my_q = qw0 + qb * 32 + r32;
         const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - j0 - 4 * g;
@@ -263,11 +283,23 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][nb][i]);
       mx = fmaxf(mx, swap_halves(mx));
-      const float m_new = fmaxf(m[qb], mx * p.c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;  // never (-inf) - (-inf)
-      moved |= m_new != m[qb];
-      alpha[qb] = exp2_fast(m[qb] - m_use);
-      m[qb] = m_new;
+      m_cand[qb] = fmaxf(m[qb], mx * p.c);
+      moved |= m_cand[qb] > m[qb] + kSlack;
+    }
+    // The running max only moves when some row's max grew by more than
+    // kSlack: below that, probabilities 2^(t - m) stay <= 2^kSlack, exact
+    // in fp32/bf16 range, and O = acc / l is unchanged because acc and l
+    // share the same reference m.
+    const bool rescale = __builtin_amdgcn_ballot_w64(moved) != 0;  // wave-uniform
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      if (rescale) {
+        const float mu = (m_cand[qb] == -INFINITY) ? 0.f : m_cand[qb];  // never (-inf) - (-inf)
+        alpha[qb] = exp2_fast(m[qb] - mu);
+        l[qb] *= alpha[qb];
+        m[qb] = m_cand[qb];
+      }
+      const float m_use = (m[qb] == -INFINITY) ? 0.f : m[qb];
       float rs = 0.f;
 #pragma unroll
       for (int nb = 0; nb < BN / 32; ++nb)
@@ -277,7 +309,7 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
           s[qb][nb][i] = pv;
           rs += pv;
         }
-      l[qb] = fmaf(l[qb], alpha[qb], rs);
+      l[qb] += rs;
     }
 
     // P^T as B operands: 16-key step kk takes registers 8 (kk % 2) .. +7 of
@@ -294,7 +326,7 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
         pf[qb][kk] = __builtin_bit_cast(bf16x8, w);
       }
 
-    if (__builtin_amdgcn_ballot_w64(moved) != 0) {  // wave-uniform: some row max moved
+    if (rescale) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -306,13 +338,8 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int kk = 0; kk < BN / 16; ++kk) {
-        i16x4 v0, v1;
-        {
-          const uint32_t c0 = (uint32_t)(((4 * dt + vcol) ^ vsw[0]) * 16);
-          const uint32_t c1 = (uint32_t)(((4 * dt + vcol) ^ vsw[1]) * 16);
-          v0 = ds_read_tr(vst + kk * 16 * D * 2 + v_rd[0] + c0);
-          v1 = ds_read_tr(vst + kk * 16 * D * 2 + v_rd[1] + c1);
-        }
+        const i16x4 v0 = ds_read_tr(stg + v_off[dt][0] + kk * 16 * D * 2);
+        const i16x4 v1 = ds_read_tr(stg + v_off[dt][1] + kk * 16 * D * 2);
         // registers 0..3: keys 4 g + r; 4..7: keys 8 + 4 g + r (of block kk)
         const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
@@ -320,7 +347,25 @@ __global__ __launch_bounds__(C::THREADS) void fwd_bf16_kernel(FwdParams p) {
         for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma32x32x16(va, pf[qb][kk], acc[qb][dt]);
       }
     }
+  };
+
+  int nt_w = ntiles;
+  int nt_full = p.Nk / BN;
+  if (p.causal) {
+    nt_w = min(ntiles, (qw0 + 32 * QB - 1) / BN + 1);  // tiles holding a key <= this wave's last row
+    nt_full = min(nt_full, (qw0 + 1) / BN);            // tiles entirely <= this wave's first row
   }
+  nt_full = min(nt_full, nt_w);
+  int t = 0;
+  for (; t < nt_full; ++t) {
+    sync_tile(t);
+    compute_tile(t, std::false_type{});
+  }
+  for (; t < nt_w; ++t) {
+    sync_tile(t);
+    compute_tile(t, std::true_type{});
+  }
+  for (; t < ntiles; ++t) sync_tile(t);
 
   // ---- epilogue: combine the two lane halves' sums, normalise once
 #pragma unroll
@@ -370,15 +415,26 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile-shape override for tuning (FA_FWD_VARIANT=1 selects the 8-wave,
+// 3-stage d=128 shape); read once per process.
+int variant() {
+  static const int v = [] {
+    const char* e = getenv("FA_FWD_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 }  // namespace
 
 bool fwd_bf16_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
-    case 64: return launch<Cfg<64, 64, 8, 1, 3>>(a, stream);
-    case 128: return launch<Cfg<128, 64, 8, 1, 3>>(a, stream);
-    case 256: return launch<Cfg<256, 32, 4, 1, 3>>(a, stream);
+    case 64: return launch<Cfg<64, 64, 4, 1, 2, 2>>(a, stream);
+    case 128: return variant() == 1 ? launch<Cfg<128, 64, 8, 1, 3, 2>>(a, stream)
+                                    : launch<Cfg<128, 64, 4, 1, 2, 2>>(a, stream);
+    case 256: return launch<Cfg<256, 32, 4, 1, 3, 1>>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
