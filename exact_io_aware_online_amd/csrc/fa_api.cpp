@@ -88,16 +88,21 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs
       num_cus = 256;
     }
   }
-  if (wgs_per_cu <= 0) wgs_per_cu = 2;
-  // Workgroups of about half the splits hold keys when lengths spread over
-  // the capacity, so aim the total at twice the resident target.
-  const long target = 2L * num_cus * wgs_per_cu;
+  if (wgs_per_cu <= 0) wgs_per_cu = 3;
+  // Splits of about 512 keys keep each decode wavefront's stream long
+  // enough to amortise its pipeline start, and enough of them give every
+  // CU `wgs_per_cu` resident wavefronts.
+  const long by_len = (capacity + 511) / 512;
   const long pairs = (long)B * Hkv;
-  long s = (target + pairs - 1) / pairs;
-  const long max_s = (capacity + 63) / 64;  // at least one 64-key tile per split
+  const long by_fill = ((long)num_cus * wgs_per_cu + pairs - 1) / pairs;
+  long s = by_len > by_fill ? by_len : by_fill;
+  // beyond ~64 waves per resident slot the extra splits only add combine work
+  const long max_waves = 64L * num_cus * wgs_per_cu;
+  if (pairs * s > max_waves) s = max_waves / pairs;
+  const long max_s = (capacity + 63) / 64;  // at least one 64-key block per split
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
-  if (s > 1024) s = 1024;
+  if (s > 65535) s = 65535;
   return (int)s;
 }
 

@@ -6,36 +6,39 @@
 // in parallel, and a second kernel merges their partial results
 // (pyshine.com FlashAttention code tour, "Why You Need This").
 //
-// Split kernel: workgroup (split s, key/value head h, sequence b) serves all
-// G = Hq / Hkv query heads that read head h, so each cache byte is read
-// once. Its 64-key tiles are staged through LDS (K row-major, V transposed)
-// by all four wavefronts; wavefront w takes keys 16w .. 16w+15 of each tile
-// and keeps its own online-softmax state (FlashAttention: Part 2, section
-// 6.2). Scores use S^T = K Q^T on the 16x16x32 bf16 MFMA with the G query
-// heads as columns (the other 16 - G columns are zero); the accumulator
-// layout is exactly the B-operand layout of the 16x16x16 MFMA, so P^T feeds
-// O^T += V^T P^T straight from registers. At the end the four wavefronts'
-// states merge through LDS.
+// Split kernel: one wavefront per (split s, key/value head h, sequence b)
+// serves all G = Hq / Hkv query heads that read head h, so each cache byte
+// is read once. It streams its key range through a private three-stage LDS
+// ring filled by direct-to-LDS 16-byte loads (no registers stage the
+// cache, no barrier: the wavefront waits only for its own loads) and keeps
+// one online-softmax state (FlashAttention: Part 2, section 6.2). Scores
+// are S^T = K Q^T on the 16x16x32 bf16 MFMA with the G query heads as
+// columns (the other 16 - G columns are zero); P^T then feeds
+// O^T += V^T P^T from registers, the V^T operand read from the row-major V
+// tile with ds_read_b64_tr_b16.
 //
 // Partial results: O_s (normalised, fp32) and L_s = log2 of the split's sum
 // of 2^(t) in base-2 units; an empty split is never written, the combine
 // derives from the sequence length which splits exist.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
 namespace fa {
 namespace {
 
-constexpr int kTile = 64;      // keys per LDS tile
-constexpr int kThreads = 256;  // 4 wavefronts
-constexpr int kMaxGroup = 16;  // query heads per key/value head (MFMA columns)
+constexpr int kSplitAlign = 64;  // split boundaries are multiples of this many keys
+constexpr int kMaxGroup = 16;    // query heads per key/value head (MFMA columns)
+// growth of the row maximum (base 2) tolerated before rescaling
+constexpr float kSlack = 8.f;
 
 struct DecParams {
-  const bf16* __restrict__ q;
-  const bf16* __restrict__ kc;
-  const bf16* __restrict__ vc;
+  const char* __restrict__ q;
+  const char* __restrict__ kc;
+  const char* __restrict__ vc;
   const int32_t* __restrict__ lens;
-  bf16* __restrict__ o;
+  char* __restrict__ o;
   float* __restrict__ lse;
   float* __restrict__ part_o;    // (B, Hq, S, D)
   float* __restrict__ part_lse;  // (B, Hq, S), base-2 units
@@ -47,40 +50,94 @@ __device__ __forceinline__ int seq_len(const DecParams& p, int b) {
   return min(max(p.lens[b], 0), p.capacity);
 }
 
-template <int D>
-__global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
-  constexpr int KS = D + 8;       // K row stride in LDS (bf16)
-  constexpr int VS = kTile + 8;   // V^T row stride in LDS (bf16)
-  constexpr int K_ITERS = kTile * D / 8 / kThreads;
-  constexpr int V_UNITS = (kTile / 4) * (D / 8);
-  constexpr int V_ITERS = (V_UNITS + kThreads - 1) / kThreads;
-  static_assert(K_ITERS >= 1 && (kTile * D / 8) % kThreads == 0, "tile/threads mismatch");
-  __shared__ __attribute__((aligned(16))) bf16 smem[kTile * KS + D * VS];
-  bf16* Ks = smem;
-  bf16* Vt = smem + kTile * KS;
-  __shared__ float red_m[4][kMaxGroup];
-  __shared__ float red_l[4][kMaxGroup];
+// Tile shape: T keys per tile (a multiple of the 32-key MFMA step) and an
+// NST-stage ring; one K (or V) tile is T * D * 2 bytes, moved by
+// DMA = T * D * 2 / 1024 direct-to-LDS loads per lane.
+template <int D, int T_, int NST_>
+struct DecTile {
+  static constexpr int T = T_;
+  static constexpr int CPR = D / 8;              // 16-byte chunks per row
+  static constexpr int TILE = T * D * 2;         // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;
+  static constexpr int DMA = TILE / 1024;        // loads per lane per tile (K or V)
+  static constexpr int NST = NST_;               // ring depth
+  static_assert(T % 32 == 0 && TILE % 1024 == 0 && (NST - 1) * 2 * DMA <= 63, "tile shape");
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// One wavefront per (split, key/value head, sequence). The wavefront keeps
+// an NST-stage LDS ring of K/V tiles filled by direct-to-LDS loads and needs
+// no barrier: it waits for its own loads (vmcnt) before reading a stage.
+template <int D, class TL>
+__global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
+  constexpr int T = TL::T, CPR = TL::CPR, NST = TL::NST;
+  __shared__ __attribute__((aligned(1024))) char smem[NST * TL::STAGE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
+
+  const int lane = threadIdx.x;
   const int col = lane & 15;  // query head within the group (MFMA column)
   const int g4 = lane >> 4;   // lane quarter
-  const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  // the Hkv heads of one (sequence, split) are adjacent in dispatch order,
+  // so together they stream whole contiguous cache rows
+  const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
   const int L = seq_len(p, b);
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, L);
   if (start >= end && !(p.S == 1 && start == 0)) return;  // empty split: nothing to write
+  const int ntiles = end > start ? (end - start + T - 1) / T : 0;
 
   const int G = p.group;
-  const int hq = h * G + col;
-  const int64_t kv_stride = (int64_t)p.Hkv * D;
+  const int kv_row = p.Hkv * D * 2;  // bytes between cache rows
+  const char* kbase = p.kc + (((int64_t)b * p.capacity + start) * p.Hkv + h) * D * 2;
+  const char* vbase = p.vc + (((int64_t)b * p.capacity + start) * p.Hkv + h) * D * 2;
 
-  // Q^T as B operand of 16x16x32: register i of k-step ks = Q[hq][32 ks + 8 g4 + i].
+  // DMA addressing: load j of a tile fills slot 64 j + lane (row slot / CPR)
+  int dma_row[TL::DMA], dma_col[TL::DMA];
+#pragma unroll
+  for (int j = 0; j < TL::DMA; ++j) {
+    const int slot = j * 64 + lane;
+    dma_row[j] = slot / CPR;
+    dma_col[j] = ((slot % CPR) ^ swz<CPR>(slot / CPR)) * 16;
+  }
+  auto issue_tile = [&](int t) {
+    const int j0 = t * T;
+    const int last = end - start - 1 - j0;  // rows past the end re-read the last key (masked later)
+    const char* ks = kbase + (int64_t)j0 * kv_row;
+    const char* vs = vbase + (int64_t)j0 * kv_row;
+    const uint32_t st = lds0 + (uint32_t)((t % NST) * TL::STAGE);
+#pragma unroll
+    for (int j = 0; j < TL::DMA; ++j)
+      dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < TL::DMA; ++j)
+      dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
+  };
+#pragma unroll
+  for (int t = 0; t < NST - 1; ++t)
+    if (t < ntiles) issue_tile(t);
+
+  // Q^T as B operand of 16x16x32: register i of k-step ks = Q[h G + col][32 ks + 8 g4 + i]
   bf16x8 qf[D / 32];
   {
-    const bf16* qrow = p.q + ((int64_t)b * p.Hq + hq) * D;
+    const char* qrow = p.q + ((int64_t)b * p.Hq + h * G + col) * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = col < G ? *reinterpret_cast<const bf16x8*>(qrow + ks * 32 + g4 * 8) : bf16x8{};
+      qf[ks] = col < G ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 32 + g4 * 8) * 2) : bf16x8{};
+  }
+
+  // per-lane LDS offsets within a stage
+  uint32_t k_off[D / 32];
+  {
+    const int sw = swz<CPR>(col);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) k_off[ks] = (uint32_t)(col * D * 2 + (((4 * ks + g4) ^ sw) * 16));
+  }
+  uint32_t v_off[D / 16];
+  {
+    const int row = 4 * g4 + (col >> 2);
+    const int sw = swz<CPR>(row);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      v_off[dt] = (uint32_t)(TL::TILE + row * D * 2 + (col & 1) * 8 + (((2 * dt + ((col & 3) >> 1)) ^ sw) * 16));
   }
 
   f32x4 acc[D / 16];
@@ -88,157 +145,123 @@ __global__ __launch_bounds__(kThreads) void decode_split_kernel(DecParams p) {
   for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
   float m = -INFINITY, l = 0.f;
 
-  const bf16* kbase = p.kc + (int64_t)b * p.capacity * kv_stride + (int64_t)h * D;
-  const bf16* vbase = p.vc + (int64_t)b * p.capacity * kv_stride + (int64_t)h * D;
-  u32x4 kreg[K_ITERS];
-  u32x4 vreg[V_ITERS][4];
-
-  auto load_tile = [&](int j0) {
+  auto compute_tile = [&](int t, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint32_t stg = lds0 + (uint32_t)((t % NST) * TL::STAGE);
+    // S^T: T keys x 16 columns, lane (col, g4) holds keys 16 tb + 4 g4 + i
+    f32x4 sc[T / 16];
 #pragma unroll
-    for (int it = 0; it < K_ITERS; ++it) {
-      const int c = tid + it * kThreads;
-      const int row = c / (D / 8), cc = c % (D / 8);
-      const int key = j0 + row;
-      kreg[it] = key < end ? load_u32x4(kbase + (int64_t)key * kv_stride + cc * 8) : u32x4{0, 0, 0, 0};
-    }
+    for (int tb = 0; tb < T / 16; ++tb) {
+      sc[tb] = f32x4{};
 #pragma unroll
-    for (int it = 0; it < V_ITERS; ++it) {
-      const int u = tid + it * kThreads;
-      const int kg = u % (kTile / 4), dc = u / (kTile / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = j0 + kg * 4 + r;
-        vreg[it][r] = (u < V_UNITS && key < end) ? load_u32x4(vbase + (int64_t)key * kv_stride + dc * 8)
-                                                 : u32x4{0, 0, 0, 0};
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)(stg + k_off[ks] + tb * 16 * D * 2);
+        sc[tb] = mfma16x16x32(kf, qf[ks], sc[tb]);
       }
     }
-  };
-  auto store_tile = [&]() {
+    if constexpr (MASK) {
+      const int lim = end - start - 1 - t * T - 4 * g4;  // key offset 16 tb + i visible iff <= lim
 #pragma unroll
-    for (int it = 0; it < K_ITERS; ++it) {
-      const int c = tid + it * kThreads;
-      store_u32x4(Ks + (c / (D / 8)) * KS + (c % (D / 8)) * 8, kreg[it]);
+      for (int tb = 0; tb < T / 16; ++tb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (16 * tb + i > lim) sc[tb][i] = -INFINITY;
     }
-#pragma unroll
-    for (int it = 0; it < V_ITERS; ++it) {
-      const int u = tid + it * kThreads;
-      if (u < V_UNITS) {
-        const int kg = u % (kTile / 4), dc = u / (kTile / 4);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int w = j >> 1;
-          uint32_t lo, hi;
-          if (j & 1) {
-            lo = (vreg[it][0][w] >> 16) | (vreg[it][1][w] & 0xffff0000u);
-            hi = (vreg[it][2][w] >> 16) | (vreg[it][3][w] & 0xffff0000u);
-          } else {
-            lo = (vreg[it][0][w] & 0xffffu) | (vreg[it][1][w] << 16);
-            hi = (vreg[it][2][w] & 0xffffu) | (vreg[it][3][w] << 16);
-          }
-          *reinterpret_cast<u32x2*>(Vt + (dc * 8 + j) * VS + kg * 4) = u32x2{lo, hi};
-        }
-      }
-    }
-  };
-
-  const int ntiles = (end - start + kTile - 1) / kTile;
-  if (ntiles > 0) load_tile(start);
-  for (int t = 0; t < ntiles; ++t) {
-    const int j0 = start + t * kTile;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ntiles) load_tile(j0 + kTile);
-
-    const int kw0 = j0 + wave * 16;  // first key of this wavefront
-    if (kw0 >= end) continue;
-
-    // S^T (16 keys x 16 columns)
-    f32x4 sc = f32x4{};
-    const bf16* krow = Ks + (wave * 16 + col) * KS + g4 * 8;
-#pragma unroll
-    for (int ks = 0; ks < D / 32; ++ks) {
-      const bf16x8 kf = *reinterpret_cast<const bf16x8*>(krow + ks * 32);
-      sc = mfma16x16x32(kf, qf[ks], sc);
-    }
-    // lane (col, g4) holds keys kw0 + 4 g4 + i
     float mx = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (kw0 + 4 * g4 + i >= end) sc[i] = -INFINITY;
-      mx = fmaxf(mx, sc[i]);
-    }
+    for (int tb = 0; tb < T / 16; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tb][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m, mx * p.c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = exp2_fast(m - m_use);
-    m = m_new;
+    const float m_cand = fmaxf(m, mx * p.c);
+    // move the reference max only when it grew by more than kSlack (see the
+    // prefill kernel: O = acc / l does not depend on the reference)
+    const bool rescale = __builtin_amdgcn_ballot_w64(m_cand > m + kSlack) != 0;
+    float alpha = 1.f;
+    if (rescale) {
+      const float mu = (m_cand == -INFINITY) ? 0.f : m_cand;
+      alpha = exp2_fast(m - mu);
+      l *= alpha;
+      m = m_cand;
+    }
+    const float m_use = (m == -INFINITY) ? 0.f : m;
     float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = exp2_fast(fmaf(sc[i], p.c, -m_use));
-      rs += sc[i];
-    }
-    l = fmaf(l, alpha, rs);
-    i16x4 pf;
-    {
-      const uint32_t w0 = pack_bf16x2(sc[0], sc[1]), w1 = pack_bf16x2(sc[2], sc[3]);
-      pf = __builtin_bit_cast(i16x4, u32x2{w0, w1});
-    }
+    for (int tb = 0; tb < T / 16; ++tb)
 #pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) {
-      acc[dt] *= alpha;
-      const i16x4 vf = *reinterpret_cast<const i16x4*>(Vt + (dt * 16 + col) * VS + wave * 16 + g4 * 4);
-      acc[dt] = mfma16x16x16(vf, pf, acc[dt]);
+      for (int i = 0; i < 4; ++i) {
+        sc[tb][i] = exp2_fast(fmaf(sc[tb][i], p.c, -m_use));
+        rs += sc[tb][i];
+      }
+    l += rs;
+    // branch-free (alpha is 1 when nothing moved): keeps the accumulator's
+    // loop-carried registers free of conditional copies
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+    // O^T += V^T P^T over 32-key steps: registers 0..3 hold keys 32 kk + 4 g4 + r,
+    // 4..7 keys 32 kk + 16 + 4 g4 + r
+#pragma unroll
+    for (int kk = 0; kk < T / 32; ++kk) {
+      u32x4 w;
+      w[0] = pack_bf16x2(sc[2 * kk][0], sc[2 * kk][1]);
+      w[1] = pack_bf16x2(sc[2 * kk][2], sc[2 * kk][3]);
+      w[2] = pack_bf16x2(sc[2 * kk + 1][0], sc[2 * kk + 1][1]);
+      w[3] = pack_bf16x2(sc[2 * kk + 1][2], sc[2 * kk + 1][3]);
+      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        const i16x4 v0 = ds_read_tr(stg + v_off[dt] + kk * 32 * D * 2);
+        const i16x4 v1 = ds_read_tr(stg + v_off[dt] + (kk * 32 + 16) * D * 2);
+        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pf, acc[dt]);
+      }
     }
+  };
+
+  auto wait_tile = [&](int t) {
+    // loads issued after tile t: tiles t+1 .. min(t+NST-1, ntiles-1)
+    const int after = min(NST - 1, ntiles - 1 - t);
+    if (after >= 3) wait_vmcnt<(NST >= 4 ? 6 * TL::DMA : 0)>();
+    else if (after == 2) wait_vmcnt<(NST >= 3 ? 4 * TL::DMA : 0)>();
+    else if (after == 1) wait_vmcnt<2 * TL::DMA>();
+    else wait_vmcnt<0>();
+  };
+
+  int t = 0;
+  const int nfull = (end - start) / T;  // tiles with every key valid
+  for (; t < nfull; ++t) {
+    if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
+    wait_tile(t);
+    compute_tile(t, std::false_type{});
+  }
+  for (; t < ntiles; ++t) {
+    if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
+    wait_tile(t);
+    compute_tile(t, std::true_type{});
   }
 
-  // Merge the four wavefronts: sum l over lane quarters, then across waves.
+  // epilogue: sum l over the lane quarters, normalise, write
   l += __shfl_xor(l, 16, 64);
   l += __shfl_xor(l, 32, 64);
-  if (g4 == 0 && col < kMaxGroup) {
-    red_m[wave][col] = m;
-    red_l[wave][col] = l;
-  }
-  __syncthreads();  // also: every wave is done with the K/V tiles
-  float* red_o = reinterpret_cast<float*>(smem);  // reuse the tile memory: 4 x 16 x D floats
-  static_assert(4 * kMaxGroup * D * 4 <= (kTile * KS + D * VS) * 2, "merge buffer too small");
-  float M = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) M = fmaxf(M, red_m[w][col]);
-  const float Mu = (M == -INFINITY) ? 0.f : M;
-  const float my_w = exp2_fast(m - Mu);
-  // lane (col, g4) holds O^T[d = 16 dt + 4 g4 + i][col]
-#pragma unroll
-  for (int dt = 0; dt < D / 16; ++dt)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red_o[(wave * kMaxGroup + col) * D + dt * 16 + 4 * g4 + i] = acc[dt][i] * my_w;
-  __syncthreads();
-
-  // Thread layout for the output: query column qc, dimensions d..d+dstep.
-  const int total = G * D;
-  for (int e = tid; e < total; e += kThreads) {
-    const int qc = e / D, d = e % D;
-    float Mq = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) Mq = fmaxf(Mq, red_m[w][qc]);
-    const float Mqu = (Mq == -INFINITY) ? 0.f : Mq;
-    float lsum = 0.f, osum = 0.f;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      lsum = fmaf(red_l[w][qc], exp2_fast(red_m[w][qc] - Mqu), lsum);
-      osum += red_o[(w * kMaxGroup + qc) * D + d];
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    const int hq_out = h * G + qc;
-    const int64_t row = (int64_t)b * p.Hq + hq_out;
+  if (col < G) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const int64_t row = (int64_t)b * p.Hq + h * G + col;
     if (p.S == 1) {
-      p.o[row * D + d] = (bf16)(osum * inv);
-      if (d == 0 && p.lse != nullptr) p.lse[row] = lsum > 0.f ? (Mq + log2_fast(lsum)) * kLn2 : -INFINITY;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) {
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[dt][0] * inv, acc[dt][1] * inv);
+        w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
+        *reinterpret_cast<u32x2*>(p.o + (row * D + dt * 16 + 4 * g4) * 2) = w;
+      }
+      if (g4 == 0 && p.lse != nullptr) p.lse[row] = l > 0.f ? (m + log2_fast(l)) * kLn2 : -INFINITY;
     } else {
-      p.part_o[(row * p.S + s) * D + d] = osum * inv;
-      if (d == 0) p.part_lse[row * p.S + s] = lsum > 0.f ? Mq + log2_fast(lsum) : -INFINITY;
+      float* po = p.part_o + (row * p.S + s) * D;
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt)
+        *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g4) = acc[dt] * inv;
+      if (g4 == 0) p.part_lse[row * p.S + s] = l > 0.f ? m + log2_fast(l) : -INFINITY;
     }
   }
 }
@@ -271,18 +294,18 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int ro
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
-  for (int e = 0; e < PER; ++e) p.o[(int64_t)row * D + lane * PER + e] = (bf16)(o[e] * inv);
+  for (int e = 0; e < PER; ++e) reinterpret_cast<bf16*>(p.o)[(int64_t)row * D + lane * PER + e] = (bf16)(o[e] * inv);
   if (lane == 0 && p.lse != nullptr) p.lse[row] = wsum > 0.f ? (Mu + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
-template <int D>
+template <int D, class TL>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   DecParams p;
-  p.q = static_cast<const bf16*>(a.q);
-  p.kc = static_cast<const bf16*>(a.kcache);
-  p.vc = static_cast<const bf16*>(a.vcache);
+  p.q = static_cast<const char*>(a.q);
+  p.kc = static_cast<const char*>(a.kcache);
+  p.vc = static_cast<const char*>(a.vcache);
   p.lens = a.seqlens;
-  p.o = static_cast<bf16*>(a.o);
+  p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
@@ -297,8 +320,8 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     p.part_o = static_cast<float*>(a.workspace);
     p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;
   }
-  dim3 grid(p.S, a.Hkv, a.B);
-  hipLaunchKernelGGL((decode_split_kernel<D>), grid, dim3(kThreads), 0, stream, p);
+  dim3 grid(a.Hkv, p.S, a.B);
+  hipLaunchKernelGGL((decode_split_kernel<D, TL>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
   const int rows = a.B * a.Hq;
@@ -310,8 +333,8 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 int decode_chunk(int capacity, int num_splits) {
   const int per = (capacity + num_splits - 1) / num_splits;
-  const int c = ((per + kTile - 1) / kTile) * kTile;
-  return c > 0 ? c : kTile;
+  const int c = ((per + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
+  return c > 0 ? c : kSplitAlign;
 }
 
 size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
@@ -325,9 +348,9 @@ bool decode_supported(int d, int group) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.d) {
-    case 64: return launch<64>(a, stream);
-    case 128: return launch<128>(a, stream);
-    case 256: return launch<256>(a, stream);
+    case 64: return launch<64, DecTile<64, 64, 3>>(a, stream);
+    case 128: return launch<128, DecTile<128, 32, 3>>(a, stream);
+    case 256: return launch<256, DecTile<256, 32, 2>>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -69,4 +69,44 @@ __device__ __forceinline__ void store_u32x4(void* p, const u32x4& v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
 
+#define LDS3 __attribute__((address_space(3)))
+
+// Chunk swizzle of a tile row: physical chunk = logical chunk ^ swz(row).
+// For rows of 16+ chunks the swizzle depends on row % 16 and spreads the
+// 16 consecutive rows a b128 read touches over 16 chunks; pairs of
+// consecutive rows (4 rows per transposed read) land on disjoint chunk pairs.
+// Rows of 8 chunks (d = 64) are 128 bytes, two per 256-byte bank line, so
+// the swizzle follows row / 2 and the row parity supplies the other half.
+template <int CPR>
+__device__ __forceinline__ int swz(int row) {
+  if constexpr (CPR >= 16) {
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 3) << 1) | ((x >> 2) & 1);
+  }
+}
+
+// One 16-byte direct-to-LDS load per lane: lane l's bytes land at
+// lds_addr + 16 l (lds_addr wave-uniform, in M0).
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :: "v"(voff), "s"(sbase), "s"(lds_addr) : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ void barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 i16x4*)(uintptr_t)lds_addr);
+}
+
 }  // namespace fa
