@@ -48,8 +48,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_F32) return FA_ERR_UNSUPPORTED;
   const bool supported = dtype == FA_DTYPE_BF16 ? fa::fwd_bf16_supported(d) : fa::fwd_f32_supported(d);
   if (!supported) return FA_ERR_UNSUPPORTED;
-  // grid limits: y = Hq, z = B
-  if (Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  // the prefill grid is one dimension of ceil(Nq / 64) * Hq * B workgroups at most
+  if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;

@@ -47,7 +47,7 @@ struct FwdParams {
   const char* __restrict__ v;
   char* __restrict__ o;
   float* __restrict__ lse;
-  int Nq, Nk, Hq, Hkv, group;
+  int Nq, Nk, Hq, Hkv, group, B;
   int causal;
   int n_qtiles;
   float c;  // scale * log2(e)
@@ -84,11 +84,22 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   const int g = lane >> 5;    // half of the wavefront
   const int r32 = lane & 31;  // query (S^T column) within a 32-row block
 
-  int qt = blockIdx.x;
-  if (p.causal) qt = p.n_qtiles - 1 - qt;  // longest rows first
-  const int hq = blockIdx.y;
-  const int b = blockIdx.z;
-  const int kvh = hq / p.group;
+  // Work order (1-D grid): rank r of the query tile is outermost, so with a
+  // causal mask every head's longest tile is dispatched before any shorter
+  // one (longest-processing-time order; the short tiles fill the tail).
+  // Within a rank, workgroups that share a key/value head sit a multiple of
+  // Hkv * B apart; with Hkv * B a multiple of the 8 XCDs (dispatch goes
+  // round-robin over them) they land on the same XCD and share its L2.
+  const int heads = p.Hq * p.B;
+  const int r = blockIdx.x / heads;
+  const int rest = blockIdx.x - r * heads;
+  const int pairs = p.Hkv * p.B;
+  const int j = rest / pairs;
+  const int pr = rest - j * pairs;
+  const int b = pr / p.Hkv;
+  const int kvh = pr - b * p.Hkv;
+  const int hq = kvh * p.group + j;
+  const int qt = p.causal ? p.n_qtiles - 1 - r : r;
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32 * QB;  // first query row of this wavefront
 
@@ -370,7 +381,8 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.causal = a.causal;
   p.n_qtiles = (a.Nq + C::BM - 1) / C::BM;
   p.c = a.scale * kLog2e;
-  dim3 grid(p.n_qtiles, a.Hq, a.B);
+  p.B = a.B;
+  dim3 grid(p.n_qtiles * a.Hq * a.B);
   hipLaunchKernelGGL((fwd_bf16_kernel<C>), grid, dim3(C::THREADS), 0, stream, p);
   return hipGetLastError();
 }
