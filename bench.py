@@ -104,6 +104,9 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (outside the timed "
+                         "region) as the known-size reference for HBM byte counters")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -148,6 +151,14 @@ def main():
         fa.fa_fwd_kvcache(qd, kc, vc, lens, o=od, lse=lsed, num_splits=S, scale=scale_d, workspace=ws)
         if ev is not None:
             ev[2].record()
+
+    if args.copy_calibration_mib > 0:
+        src = torch.empty(args.copy_calibration_mib << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
