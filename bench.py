@@ -97,8 +97,10 @@ def cpu_baseline(name, w, budget_s=12.0):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # The GPU's clocks take on the order of a second of sustained work to
+    # settle; the default warmup (~1 s of steps) lets them before timing.
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--prefill", default=DEFAULT_PREFILL)
     ap.add_argument("--decode", default=DEFAULT_DECODE)
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library default)")

@@ -123,6 +123,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
     for (int ks = 0; ks < D / 32; ++ks)
       qf[ks] = col < G ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 32 + g4 * 8) * 2) : bf16x8{};
   }
+  wait_vm_loads();
 
   // per-lane LDS offsets within a stage
   uint32_t k_off[D / 32];

@@ -19,6 +19,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace fa {
 
 typedef __bf16 bf16;
@@ -62,6 +65,32 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max / sum of x over lanes l and l ^ 32, in both lanes. v_permlane32_swap
+// exchanges the upper half of one register with the lower half of another;
+// applied to two copies of x it leaves x[l] in one result and x[l ^ 32] in
+// the other (which is which does not matter to a symmetric reduction), with
+// no LDS round trip.
+__device__ __forceinline__ float halves_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1.
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 __device__ __forceinline__ u32x4 load_u32x4(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
@@ -98,6 +127,15 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
+
+// s_waitcnt vmcnt(0) issued as a builtin, which the compiler's own wait
+// insertion sees: after it, no load into registers issued earlier counts as
+// outstanding. Without it the compiler waits for such a load (the Q
+// fragment) at its first use inside the tile loop with vmcnt(0) on every
+// iteration, which also drains the direct-to-LDS prefetches it cannot see.
+// Encoding (gfx9): vmcnt [3:0] and [15:14] = 0, expcnt [6:4] = 7,
+// lgkmcnt [11:8] = 15 (no wait on those).
+__device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");

@@ -33,6 +33,8 @@
 // written as ln2 * (m + log2 l).
 #include <type_traits>
 
+#include <stdlib.h>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -55,6 +57,9 @@ template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_, QB = QB_, NST = NST_;
   static constexpr int WAVES_PER_SIMD = WPS_;  // register budget: 512 / WPS per lane
+  // ring stage as an immediate LDS offset (one copy of the tile code per
+  // stage); head dimension 256 has no registers to spare for it
+  static constexpr bool CONST_STAGE = D_ < 256;
   static constexpr int BM = NW * 32 * QB;          // query rows per workgroup
   static constexpr int THREADS = NW * 64;
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
@@ -111,31 +116,37 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   // ---- DMA addressing: load j of a tile fills slot j*THREADS + tid
   const char* kbase = p.k + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
   const char* vbase = p.v + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  // load j of a tile fills slot s = j*THREADS + tid, i.e. row s / CPR; the
+  // byte offsets of full tiles are computed once
   int dma_row[C::DMA], dma_col[C::DMA];
+  uint32_t dma_off[C::DMA];
 #pragma unroll
   for (int j = 0; j < C::DMA; ++j) {
     const int slot = j * C::THREADS + tid;
-    const int row = slot / CPR;
-    dma_row[j] = row;
-    dma_col[j] = ((slot % CPR) ^ swz<CPR>(row)) * 16;
+    dma_row[j] = slot / CPR;
+    dma_col[j] = ((slot % CPR) ^ swz<CPR>(slot / CPR)) * 16;
+    dma_off[j] = (uint32_t)(dma_row[j] * kv_row + dma_col[j]);
   }
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
 
   auto issue_tile = [&](int t) {
     const int j0 = t * BN;
-    const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
     const char* ks = kbase + (int64_t)j0 * kv_row;
     const char* vs = vbase + (int64_t)j0 * kv_row;
     const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::STAGE_BYTES);
+    if (j0 + BN <= p.Nk) {  // uniform: full tile
 #pragma unroll
-    for (int j = 0; j < C::DMA; ++j) {
-      const uint32_t off = (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]);
-      dma16(ks, off, st + j * C::THREADS * 16);
-    }
+      for (int j = 0; j < C::DMA; ++j) dma16(ks, dma_off[j], st + j * C::THREADS * 16);
 #pragma unroll
-    for (int j = 0; j < C::DMA; ++j) {
-      const uint32_t off = (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]);
-      dma16(vs, off, st + C::TILE_BYTES + j * C::THREADS * 16);
+      for (int j = 0; j < C::DMA; ++j) dma16(vs, dma_off[j], st + C::TILE_BYTES + j * C::THREADS * 16);
+    } else {
+      const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
+#pragma unroll
+      for (int j = 0; j < C::DMA; ++j)
+        dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * C::THREADS * 16);
+#pragma unroll
+      for (int j = 0; j < C::DMA; ++j)
+        dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + C::TILE_BYTES + j * C::THREADS * 16);
     }
   };
 
@@ -155,6 +166,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       qf[qb][ks] = row < p.Nq ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
+  wait_vm_loads();
 
   f32x16 acc[QB][D / 32];
 #pragma unroll
@@ -209,25 +221,35 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
   };
 
-  auto compute_tile = [&](int t, auto mask_tag) {
+  // compute on tile t held in ring stage `stage`; given as a compile-time
+  // constant, every LDS read address is a per-lane register plus an immediate
+  auto compute_tile = [&](int t, auto mask_tag, auto stage) {
     constexpr bool MASK = decltype(mask_tag)::value;
+    const uint32_t stg = (uint32_t)(int)stage * C::STAGE_BYTES;
     const int j0 = t * BN;
-    const uint32_t stg = lds0 + (uint32_t)((t % NST) * C::STAGE_BYTES);
 
-    // S^T = K Q^T: BN keys x 32 queries per query block
-    f32x16 s[QB][BN / 32];
+    // S^T = K Q^T: BN keys x 32 queries per query block. The K operands
+    // are read KPF ahead of their MFMA so the LDS latency overlaps the chain.
+    constexpr int NBT = BN / 32;
+    constexpr int NK = (D / 16) * NBT;
+    constexpr int KPF = D >= 256 ? 2 : (NK < 8 ? NK : 8);
+    auto kread = [&](int i) {
+      return *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + k_off[i / NBT] + (i % NBT) * 32 * D * 2);
+    };
+    f32x16 s[QB][NBT];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int nb = 0; nb < BN / 32; ++nb) s[qb][nb] = f32x16{};
+      for (int nb = 0; nb < NBT; ++nb) s[qb][nb] = f32x16{};
+    bf16x8 kf[NK];
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
+    for (int i = 0; i < KPF; ++i) kf[i] = kread(i);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the chain
 #pragma unroll
-      for (int nb = 0; nb < BN / 32; ++nb) {
-        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)(stg + k_off[ks] + nb * 32 * D * 2);
+    for (int i = 0; i < NK; ++i) {
+      if (i + KPF < NK) kf[i + KPF] = kread(i + KPF);
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s[qb][nb] = mfma32x32x16(kf, qf[qb][ks], s[qb][nb]);
-      }
+      for (int qb = 0; qb < QB; ++qb) s[qb][i % NBT] = mfma32x32x16(kf[i], qf[qb][i / NBT], s[qb][i % NBT]);
     }
 
     bool moved = false;
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         const int my_q = qw0 + qb * 32 + r32;
         const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - j0 - 4 * g;
 #pragma unroll
-        for (int nb = 0; nb < BN / 32; ++nb)
+        for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int off = nb * 32 + 8 * (i >> 2) + (i & 3);
@@ -248,10 +270,10 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int nb = 0; nb < BN / 32; ++nb)
+      for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][nb][i]);
-      mx = fmaxf(mx, swap_halves(mx));
+      mx = halves_max(mx);
       m_cand[qb] = fmaxf(m[qb], mx * p.c);
       moved |= m_cand[qb] > m[qb] + kSlack;
     }
@@ -269,16 +291,21 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         m[qb] = m_cand[qb];
       }
       const float m_use = (m[qb] == -INFINITY) ? 0.f : m[qb];
-      float rs = 0.f;
+      // row sum as a pairwise tree: a short dependency chain
+      float e[NBT * 16];
 #pragma unroll
-      for (int nb = 0; nb < BN / 32; ++nb)
+      for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float pv = exp2_fast(fmaf(s[qb][nb][i], p.c, -m_use));
           s[qb][nb][i] = pv;
-          rs += pv;
+          e[nb * 16 + i] = pv;
         }
-      l[qb] += rs;
+#pragma unroll
+      for (int w = NBT * 16 / 2; w >= 1; w /= 2)
+#pragma unroll
+        for (int i = 0; i < w; ++i) e[i] += e[i + w];
+      l[qb] += e[0];
     }
 
     // P^T as B operands: 16-key step kk takes registers 8 (kk % 2) .. +7 of
@@ -291,7 +318,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         const int nb = kk >> 1, h = (kk & 1) * 8;
         u32x4 w;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(s[qb][nb][h + 2 * e], s[qb][nb][h + 2 * e + 1]);
+        for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(s[qb][nb][h + 2 * e2], s[qb][nb][h + 2 * e2 + 1]);
         pf[qb][kk] = __builtin_bit_cast(bf16x8, w);
       }
 
@@ -302,19 +329,38 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         for (int dt = 0; dt < D / 32; ++dt) acc[qb][dt] *= alpha[qb];
     }
 
-    // O^T += V^T P^T
+    // O^T += V^T P^T. The wavefront runs this MFMA block at raised issue
+    // priority: with two wavefronts per SIMD, one then streams its MFMAs
+    // while the other works through its softmax on the vector ALU.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
       for (int kk = 0; kk < BN / 16; ++kk) {
-        const i16x4 v0 = ds_read_tr(stg + v_off[dt][0] + kk * 16 * D * 2);
-        const i16x4 v1 = ds_read_tr(stg + v_off[dt][1] + kk * 16 * D * 2);
+        const i16x4 v0 = ds_read_tr(lds0 + stg + v_off[dt][0] + kk * 16 * D * 2);
+        const i16x4 v1 = ds_read_tr(lds0 + stg + v_off[dt][1] + kk * 16 * D * 2);
         // registers 0..3: keys 4 g + r; 4..7: keys 8 + 4 g + r (of block kk)
         const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma32x32x16(va, pf[qb][kk], acc[qb][dt]);
       }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // tile t in its ring stage t % NST (uniform), for loops whose trip count
+  // is not a multiple of NST
+  auto compute_any = [&](int t, auto mask_tag) {
+    const int st = t % NST;
+    if constexpr (C::CONST_STAGE) {
+      static_for<NST>([&](auto S) {
+        if (st == decltype(S)::value) compute_tile(t, mask_tag, S);
+      });
+    } else {
+      compute_tile(t, mask_tag, st);
     }
   };
 
@@ -326,13 +372,22 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   }
   nt_full = min(nt_full, nt_w);
   int t = 0;
+  // unmasked tiles NST at a time: tile t + S sits in stage S
+  if constexpr (C::CONST_STAGE) {
+    for (; t + NST <= nt_full; t += NST) {
+      static_for<NST>([&](auto S) {
+        sync_tile(t + decltype(S)::value);
+        compute_tile(t + decltype(S)::value, std::false_type{}, S);
+      });
+    }
+  }
   for (; t < nt_full; ++t) {
     sync_tile(t);
-    compute_tile(t, std::false_type{});
+    compute_any(t, std::false_type{});
   }
   for (; t < nt_w; ++t) {
     sync_tile(t);
-    compute_tile(t, std::true_type{});
+    compute_any(t, std::true_type{});
   }
   for (; t < ntiles; ++t) sync_tile(t);
 
@@ -340,7 +395,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int my_q = qw0 + qb * 32 + r32;
-    const float lt = l[qb] + swap_halves(l[qb]);
+    const float lt = halves_sum(l[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     if (my_q < p.Nq) {
       char* orow = p.o + ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
@@ -385,18 +440,42 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile-shape override for tuning (FA_FWD_VARIANT), read once per process.
+int variant() {
+  static const int v = [] {
+    const char* e = getenv("FA_FWD_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 }  // namespace
 
 bool fwd_bf16_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
-// Tile shapes per head dimension, chosen by measurement on MI355X: 32-key
-// tiles keep d=128 under 168 VGPRs (three waves per SIMD fit), and d=256
-// runs two waves per SIMD at the cost of a few spills rather than one.
+// Tile shapes per head dimension, chosen by measurement on MI355X: d=128
+// takes 64-key tiles at two waves per SIMD, d=256 runs two waves per SIMD
+// at the cost of a few spills rather than one.
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
-    case 64: return launch<Cfg<64, 64, 4, 1, 2, 3>>(a, stream);
-    case 128: return launch<Cfg<128, 32, 4, 1, 2, 2>>(a, stream);
-    case 256: return launch<Cfg<256, 32, 4, 1, 2, 2>>(a, stream);
+    case 64:
+      switch (variant()) {
+        case 1: return launch<Cfg<64, 64, 4, 1, 2, 2>>(a, stream);
+        case 2: return launch<Cfg<64, 128, 4, 1, 2, 2>>(a, stream);
+        default: return launch<Cfg<64, 64, 4, 1, 2, 3>>(a, stream);
+      }
+    case 128:
+      switch (variant()) {
+        case 1: return launch<Cfg<128, 32, 4, 1, 2, 2>>(a, stream);
+        case 2: return launch<Cfg<128, 64, 4, 1, 3, 2>>(a, stream);
+        default: return launch<Cfg<128, 64, 4, 1, 2, 2>>(a, stream);
+      }
+    case 256:
+      switch (variant()) {
+        case 1: return launch<Cfg<256, 64, 4, 1, 2, 1>>(a, stream);
+        case 2: return launch<Cfg<256, 32, 4, 1, 3, 1>>(a, stream);
+        default: return launch<Cfg<256, 32, 4, 1, 2, 2>>(a, stream);
+      }
     default: return hipErrorInvalidValue;
   }
 }
