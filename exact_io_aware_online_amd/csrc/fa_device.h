@@ -116,6 +116,23 @@ __device__ __forceinline__ int swz(int row) {
   }
 }
 
+// Chunk swizzle of the prefill K/V tiles. Their reads take, per LDS cycle,
+// one logical chunk of 16 consecutive rows (K, 16-byte reads) or four
+// logical chunks of 4 consecutive rows (V, transposing 8-byte reads over 32
+// lanes); both touch 64 distinct banks when the two 2-bit digits of
+// row % 16 are swapped into the chunk index. Rows of 8 chunks (d = 64) are
+// two per 256-byte bank line: there the swizzle follows row / 2 and puts
+// the two rows of a line pair into opposite halves of the row.
+template <int CPR>
+__device__ __forceinline__ int swz_pf(int row) {
+  if constexpr (CPR >= 16) {
+    return ((row & 3) << 2) | ((row >> 2) & 3);
+  } else {
+    const int x = (row >> 1) & 7;
+    return ((x & 1) << 2) | ((x >> 1) & 3);
+  }
+}
+
 // One 16-byte direct-to-LDS load per lane: lane l's bytes land at
 // lds_addr + 16 l (lds_addr wave-uniform, in M0).
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds_addr) {

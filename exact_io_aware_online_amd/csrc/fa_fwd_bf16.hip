@@ -124,7 +124,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   for (int j = 0; j < C::DMA; ++j) {
     const int slot = j * C::THREADS + tid;
     dma_row[j] = slot / CPR;
-    dma_col[j] = ((slot % CPR) ^ swz<CPR>(slot / CPR)) * 16;
+    dma_col[j] = ((slot % CPR) ^ swz_pf<CPR>(slot / CPR)) * 16;
     dma_off[j] = (uint32_t)(dma_row[j] * kv_row + dma_col[j]);
   }
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   // K (b128): row = 32 nb + r32, logical chunk 2 ks + g
   uint32_t k_off[D / 16];
   {
-    const int ksw = swz<CPR>(r32);
+    const int ksw = swz_pf<CPR>(r32);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
   }
@@ -199,7 +199,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
-      const int sw = swz<CPR>(row);
+      const int sw = swz_pf<CPR>(row);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
         v_off[dt][h] = (uint32_t)(C::TILE_BYTES + row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
