@@ -20,6 +20,8 @@
 // Partial results: O_s (normalised, fp32) and L_s = log2 of the split's sum
 // of 2^(t) in base-2 units; an empty split is never written, the combine
 // derives from the sequence length which splits exist.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "fa_device.h"
@@ -173,8 +175,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
     for (int tb = 0; tb < T / 16; ++tb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tb][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = quarters_max(mx);
     const float m_cand = fmaxf(m, mx * p.c);
     // move the reference max only when it grew by more than kSlack (see the
     // prefill kernel: O = acc / l does not depend on the reference)
@@ -243,8 +244,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   }
 
   // epilogue: sum l over the lane quarters, normalise, write
-  l += __shfl_xor(l, 16, 64);
-  l += __shfl_xor(l, 32, 64);
+  l = quarters_sum(l);
   if (col < G) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
     const int64_t row = (int64_t)b * p.Hq + h * G + col;
@@ -330,6 +330,15 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Tile-shape override for tuning (FA_DEC_VARIANT), read once per process.
+int dec_variant() {
+  static const int v = [] {
+    const char* e = getenv("FA_DEC_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
+}
+
 }  // namespace
 
 int decode_chunk(int capacity, int num_splits) {
@@ -350,7 +359,13 @@ bool decode_supported(int d, int group) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64: return launch<64, DecTile<64, 64, 3>>(a, stream);
-    case 128: return launch<128, DecTile<128, 32, 3>>(a, stream);
+    case 128:
+      switch (dec_variant()) {
+        case 1: return launch<128, DecTile<128, 32, 4>>(a, stream);
+        case 2: return launch<128, DecTile<128, 32, 2>>(a, stream);
+        case 3: return launch<128, DecTile<128, 64, 2>>(a, stream);
+        default: return launch<128, DecTile<128, 32, 3>>(a, stream);
+      }
     case 256: return launch<256, DecTile<256, 32, 2>>(a, stream);
     default: return hipErrorInvalidValue;
   }

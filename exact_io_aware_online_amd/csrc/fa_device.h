@@ -81,6 +81,21 @@ __device__ __forceinline__ float halves_sum(float x) {
   return __builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]);
 }
 
+// max / sum of x over the four lanes l, l ^ 16, l ^ 32, l ^ 48, in all four:
+// v_permlane16_swap exchanges the odd 16-lane rows of one register with the
+// even rows of another, which on two copies of x pairs each row with its
+// neighbour; the 32-lane swap then pairs the halves.
+__device__ __forceinline__ float quarters_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_max(fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1])));
+}
+__device__ __forceinline__ float quarters_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return halves_sum(__builtin_bit_cast(float, (uint32_t)r[0]) + __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 // Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1.
 template <class F, int... I>
 __device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {

@@ -211,12 +211,12 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   // need no mask. Peeling the loop this way keeps the accumulator's
   // loop-carried registers free of branches.
   auto sync_tile = [&](int t) {
-    // own loads of tile t are done when at most the later tiles' remain
-    if constexpr (NST == 3) {
-      if (t + 1 < ntiles) wait_vmcnt<2 * C::DMA>(); else wait_vmcnt<0>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // own loads of tile t are done when at most those of the tiles issued
+    // after it (t+1 .. t+NST-2, within range) remain
+    const int after = min(NST - 2, ntiles - 1 - t);
+    static_for<NST - 1>([&](auto A) {
+      if (after == decltype(A)::value) wait_vmcnt<decltype(A)::value * 2 * C::DMA>();
+    });
     barrier();  // everyone's loads of tile t landed; tile t-1 is no longer read
     if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
   };
@@ -460,14 +460,14 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64:
       switch (variant()) {
-        case 1: return launch<Cfg<64, 64, 4, 1, 2, 2>>(a, stream);
+        case 1: return launch<Cfg<64, 64, 4, 1, 4, 2>>(a, stream);
         case 2: return launch<Cfg<64, 128, 4, 1, 2, 2>>(a, stream);
         default: return launch<Cfg<64, 64, 4, 1, 2, 3>>(a, stream);
       }
     case 128:
       switch (variant()) {
-        case 1: return launch<Cfg<128, 32, 4, 1, 2, 2>>(a, stream);
-        case 2: return launch<Cfg<128, 64, 4, 1, 3, 2>>(a, stream);
+        case 1: return launch<Cfg<128, 32, 4, 1, 4, 2>>(a, stream);
+        case 2: return launch<Cfg<128, 32, 4, 1, 3, 2>>(a, stream);
         default: return launch<Cfg<128, 64, 4, 1, 2, 2>>(a, stream);
       }
     case 256:
