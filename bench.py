@@ -30,13 +30,18 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_PREFILL = "mha_bf16_causal_b8_h16_n2048_d128"
 DEFAULT_DECODE = "gqa_bf16_decode_b64_h32kv8_cap8192_d128"
-PREFILL_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_online_amd", "csrc", "fa_fwd_bf16.hip")
-DECODE_KERNEL_SOURCE = os.path.join(ROOT, "exact_io_aware_online_amd", "csrc", "fa_decode.hip")
+_CSRC = os.path.join(ROOT, "exact_io_aware_online_amd", "csrc")
+# the files a kernel's machine code depends on
+PREFILL_KERNEL_SOURCE = [os.path.join(_CSRC, f) for f in ("fa_fwd_bf16.hip", "fa_device.h", "fa_launch.h")]
+DECODE_KERNEL_SOURCE = [os.path.join(_CSRC, f) for f in ("fa_decode.hip", "fa_device.h", "fa_launch.h")]
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for path in paths:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def prefill_flops(w):

@@ -89,10 +89,11 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs
     }
   }
   if (wgs_per_cu <= 0) wgs_per_cu = 3;
-  // Splits of about 512 keys keep each decode wavefront's stream long
-  // enough to amortise its pipeline start, and enough of them give every
-  // CU `wgs_per_cu` resident wavefronts.
-  const long by_len = (capacity + 511) / 512;
+  // Splits of about 1024 keys keep each decode wavefront's stream long
+  // enough to amortise its pipeline start (measured best on MI355X against
+  // 512 and 768), and enough of them give every CU `wgs_per_cu` resident
+  // wavefronts.
+  const long by_len = (capacity + 1023) / 1024;
   const long pairs = (long)B * Hkv;
   const long by_fill = ((long)num_cus * wgs_per_cu + pairs - 1) / pairs;
   long s = by_len > by_fill ? by_len : by_fill;

@@ -78,9 +78,12 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   const int lane = threadIdx.x;
   const int col = lane & 15;  // query head within the group (MFMA column)
   const int g4 = lane >> 4;   // lane quarter
-  // the Hkv heads of one (sequence, split) are adjacent in dispatch order,
-  // so together they stream whole contiguous cache rows
-  const int h = blockIdx.x, s = blockIdx.y, b = blockIdx.z;
+  // The Hkv heads of one (sequence, split) are adjacent in dispatch order,
+  // so together they stream whole contiguous cache rows. Splits go in
+  // decreasing index: the last splits exist only for the longest sequences
+  // (or are empty and exit at once), so the tail of the launch is made of
+  // split 0 .. 1 workgroups, present and full-length for every sequence.
+  const int h = blockIdx.x, b = blockIdx.y, s = p.S - 1 - (int)blockIdx.z;
   const int L = seq_len(p, b);
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, L);
@@ -321,7 +324,7 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     p.part_o = static_cast<float*>(a.workspace);
     p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;
   }
-  dim3 grid(a.Hkv, p.S, a.B);
+  dim3 grid(a.Hkv, a.B, p.S);
   hipLaunchKernelGGL((decode_split_kernel<D, TL>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
@@ -356,6 +359,9 @@ bool decode_supported(int d, int group) {
   return (d == 64 || d == 128 || d == 256) && group >= 1 && group <= kMaxGroup;
 }
 
+// Tile shapes per head dimension, chosen by measurement on MI355X (d=128:
+// 64-key tiles in a two-stage ring, two wavefronts per CU, beat 32-key
+// tiles in three- or four-stage rings). FA_DEC_VARIANT selects the others.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64: return launch<64, DecTile<64, 64, 3>>(a, stream);
@@ -363,8 +369,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
       switch (dec_variant()) {
         case 1: return launch<128, DecTile<128, 32, 4>>(a, stream);
         case 2: return launch<128, DecTile<128, 32, 2>>(a, stream);
-        case 3: return launch<128, DecTile<128, 64, 2>>(a, stream);
-        default: return launch<128, DecTile<128, 32, 3>>(a, stream);
+        case 3: return launch<128, DecTile<128, 32, 3>>(a, stream);
+        default: return launch<128, DecTile<128, 64, 2>>(a, stream);
       }
     case 256: return launch<256, DecTile<256, 32, 2>>(a, stream);
     default: return hipErrorInvalidValue;

@@ -127,7 +127,7 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
 /* A num_splits for B sequences of at most `capacity` keys and Hkv key/value
  * heads on a device with `num_cus` compute units, each holding `wgs_per_cu`
  * resident decode wavefronts (pass 0 for either to use the current
- * device's count and 3 per CU): splits of about 512 keys, at least enough
+ * device's count and 3 per CU): splits of about 1024 keys, at least enough
  * splits to fill every resident slot, and no more than 64 split workgroups
  * per resident slot. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);

@@ -110,9 +110,9 @@ def test_workspace_size_formula():
 
 
 def test_default_splits():
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 256, 3) == 16     # ~512-key splits
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 256, 3) == 8      # ~1024-key splits
     assert fa.fa_kvcache_default_splits(1, 8, 8192, 256, 3) == 96      # fill 768 resident slots
     assert fa.fa_kvcache_default_splits(1, 1, 64, 256, 3) == 1         # one 64-key block: cannot split
     assert fa.fa_kvcache_default_splits(4096, 8, 8192, 256, 3) == 1    # capped by the slot budget
     assert fa.fa_kvcache_default_splits(0, 8, 8192, 256, 3) == 1
-    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 256, 3) == (1000000 + 511) // 512
+    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 256, 3) == (1000000 + 1023) // 1024
