@@ -64,7 +64,11 @@ struct Cfg {
   static constexpr int THREADS = NW * 64;
   static constexpr int CPR = D / 8;                // 16-byte chunks per row
   static constexpr int TILE_BYTES = BN * D * 2;    // one K (or V) tile
+  // LDS ring: the NST K tiles, then the NST V tiles, so a read's stage
+  // offset (stage * TILE_BYTES) plus its in-tile offset fits the 16-bit
+  // immediate of an LDS instruction for every stage
   static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int V_REGION = NST_ * TILE_BYTES;
   static constexpr int DMA = TILE_BYTES / (THREADS * 16);  // 16-byte loads per thread per tile
   static_assert(DMA >= 1 && TILE_BYTES % (THREADS * 16) == 0, "tile does not split over the threads");
   static_assert(BN % 32 == 0 && D % 32 == 0, "tile shapes");
@@ -129,16 +133,16 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   }
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
 
-  auto issue_tile = [&](int t) {
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
     const int j0 = t * BN;
     const char* ks = kbase + (int64_t)j0 * kv_row;
     const char* vs = vbase + (int64_t)j0 * kv_row;
-    const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::STAGE_BYTES);
+    const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::TILE_BYTES);
     if (j0 + BN <= p.Nk) {  // uniform: full tile
 #pragma unroll
       for (int j = 0; j < C::DMA; ++j) dma16(ks, dma_off[j], st + j * C::THREADS * 16);
 #pragma unroll
-      for (int j = 0; j < C::DMA; ++j) dma16(vs, dma_off[j], st + C::TILE_BYTES + j * C::THREADS * 16);
+      for (int j = 0; j < C::DMA; ++j) dma16(vs, dma_off[j], st + C::V_REGION + j * C::THREADS * 16);
     } else {
       const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
 #pragma unroll
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * C::THREADS * 16);
 #pragma unroll
       for (int j = 0; j < C::DMA; ++j)
-        dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + C::TILE_BYTES + j * C::THREADS * 16);
+        dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + C::V_REGION + j * C::THREADS * 16);
     }
   };
 
@@ -202,7 +206,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       const int sw = swz_pf<CPR>(row);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
-        v_off[dt][h] = (uint32_t)(C::TILE_BYTES + row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
+        v_off[dt][h] = (uint32_t)(C::V_REGION + row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
     }
   }
 
@@ -210,7 +214,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   // in order; it computes on tiles [0, nt_w), of which the first nt_full
   // need no mask. Peeling the loop this way keeps the accumulator's
   // loop-carried registers free of branches.
-  auto sync_tile = [&](int t) {
+  auto sync_tile = [&](int t) __attribute__((always_inline)) {
     // own loads of tile t are done when at most those of the tiles issued
     // after it (t+1 .. t+NST-2, within range) remain
     const int after = min(NST - 2, ntiles - 1 - t);
@@ -221,26 +225,25 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
   };
 
-  // compute on tile t held in ring stage `stage`; given as a compile-time
-  // constant, every LDS read address is a per-lane register plus an immediate
-  auto compute_tile = [&](int t, auto mask_tag, auto stage) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint32_t stg = (uint32_t)(int)stage * C::STAGE_BYTES;
-    const int j0 = t * BN;
+  constexpr int NBT = BN / 32;
+  f32x16 sc[QB][NBT];     // scores of a tile, from its S phase to its softmax
+  bf16x8 pf[QB][BN / 16]; // its P^T, from the softmax to its PV phase
 
-    // S^T = K Q^T: BN keys x 32 queries per query block. The K operands
-    // are read KPF ahead of their MFMA so the LDS latency overlaps the chain.
-    constexpr int NBT = BN / 32;
+  // S^T = K Q^T for tile t held in ring stage `stage` (given as a
+  // compile-time constant, every LDS read address is a per-lane register
+  // plus an immediate): BN keys x 32 queries per query block. The K
+  // operands are read KPF ahead of their MFMA so LDS latency overlaps the chain.
+  auto s_phase = [&](int t, auto stage) __attribute__((always_inline)) {
+    const uint32_t stg = (uint32_t)(int)stage * C::TILE_BYTES;
     constexpr int NK = (D / 16) * NBT;
     constexpr int KPF = D >= 256 ? 2 : (NK < 8 ? NK : 8);
-    auto kread = [&](int i) {
+    auto kread = [&](int i) __attribute__((always_inline)) {
       return *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + k_off[i / NBT] + (i % NBT) * 32 * D * 2);
     };
-    f32x16 s[QB][NBT];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int nb = 0; nb < NBT; ++nb) s[qb][nb] = f32x16{};
+      for (int nb = 0; nb < NBT; ++nb) sc[qb][nb] = f32x16{};
     bf16x8 kf[NK];
 #pragma unroll
     for (int i = 0; i < KPF; ++i) kf[i] = kread(i);
@@ -249,9 +252,15 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     for (int i = 0; i < NK; ++i) {
       if (i + KPF < NK) kf[i + KPF] = kread(i + KPF);
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb][i % NBT] = mfma32x32x16(kf[i], qf[qb][i / NBT], s[qb][i % NBT]);
+      for (int qb = 0; qb < QB; ++qb) sc[qb][i % NBT] = mfma32x32x16(kf[i], qf[qb][i / NBT], sc[qb][i % NBT]);
     }
+  };
 
+  // online softmax of tile t: mask, running max, lazy rescale of l and the
+  // accumulator, probabilities and their row sums, P^T packed to bf16
+  auto softmax_phase = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int j0 = t * BN;
     bool moved = false;
     float alpha[QB], m_cand[QB];
 #pragma unroll
@@ -265,14 +274,14 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int off = nb * 32 + 8 * (i >> 2) + (i & 3);
-            if (off > lim) s[qb][nb][i] = -INFINITY;
+            if (off > lim) sc[qb][nb][i] = -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[qb][nb][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[qb][nb][i]);
       mx = halves_max(mx);
       m_cand[qb] = fmaxf(m[qb], mx * p.c);
       moved |= m_cand[qb] > m[qb] + kSlack;
@@ -297,8 +306,8 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const float pv = exp2_fast(fmaf(s[qb][nb][i], p.c, -m_use));
-          s[qb][nb][i] = pv;
+          const float pv = exp2_fast(fmaf(sc[qb][nb][i], p.c, -m_use));
+          sc[qb][nb][i] = pv;
           e[nb * 16 + i] = pv;
         }
 #pragma unroll
@@ -310,7 +319,6 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 
     // P^T as B operands: 16-key step kk takes registers 8 (kk % 2) .. +7 of
     // accumulator kk / 2 (keys 8 (i / 4) + 4 g + i % 4 of that half).
-    bf16x8 pf[QB][BN / 16];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -318,7 +326,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         const int nb = kk >> 1, h = (kk & 1) * 8;
         u32x4 w;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(s[qb][nb][h + 2 * e2], s[qb][nb][h + 2 * e2 + 1]);
+        for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(sc[qb][nb][h + 2 * e2], sc[qb][nb][h + 2 * e2 + 1]);
         pf[qb][kk] = __builtin_bit_cast(bf16x8, w);
       }
 
@@ -328,12 +336,11 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
         for (int dt = 0; dt < D / 32; ++dt) acc[qb][dt] *= alpha[qb];
     }
+  };
 
-    // O^T += V^T P^T. The wavefront runs this MFMA block at raised issue
-    // priority: with two wavefronts per SIMD, one then streams its MFMAs
-    // while the other works through its softmax on the vector ALU.
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_setprio(1);
+  // O^T += V^T P^T for tile t held in ring stage `stage`
+  auto pv_phase = [&](int t, auto stage) __attribute__((always_inline)) {
+    const uint32_t stg = (uint32_t)(int)stage * C::TILE_BYTES;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -347,13 +354,24 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma32x32x16(va, pf[qb][kk], acc[qb][dt]);
       }
     }
+  };
+
+  // the whole tile in one wavefront: S, softmax, then the PV block at
+  // raised issue priority: with two wavefronts per SIMD, one then streams
+  // its MFMAs while the other works through its softmax on the vector ALU.
+  auto compute_tile = [&](int t, auto mask_tag, auto stage) __attribute__((always_inline)) {
+    s_phase(t, stage);
+    softmax_phase(t, mask_tag);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(1);
+    pv_phase(t, stage);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(0);
   };
 
   // tile t in its ring stage t % NST (uniform), for loops whose trip count
   // is not a multiple of NST
-  auto compute_any = [&](int t, auto mask_tag) {
+  auto compute_any = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     const int st = t % NST;
     if constexpr (C::CONST_STAGE) {
       static_for<NST>([&](auto S) {
