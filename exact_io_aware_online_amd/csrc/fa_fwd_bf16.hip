@@ -478,14 +478,16 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64:
       switch (variant()) {
-        case 1: return launch<Cfg<64, 64, 4, 1, 4, 2>>(a, stream);
-        case 2: return launch<Cfg<64, 128, 4, 1, 2, 2>>(a, stream);
+        case 1: return launch<Cfg<64, 64, 4, 2, 2, 2>>(a, stream);
+        case 2: return launch<Cfg<64, 32, 4, 2, 2, 2>>(a, stream);
+        case 3: return launch<Cfg<64, 64, 8, 1, 2, 2>>(a, stream);
         default: return launch<Cfg<64, 64, 4, 1, 2, 3>>(a, stream);
       }
     case 128:
       switch (variant()) {
-        case 1: return launch<Cfg<128, 32, 4, 1, 4, 2>>(a, stream);
-        case 2: return launch<Cfg<128, 32, 4, 1, 3, 2>>(a, stream);
+        case 1: return launch<Cfg<128, 64, 8, 1, 2, 2>>(a, stream);
+        case 2: return launch<Cfg<128, 32, 8, 1, 2, 2>>(a, stream);
+        case 3: return launch<Cfg<128, 64, 8, 1, 3, 2>>(a, stream);
         default: return launch<Cfg<128, 64, 4, 1, 2, 2>>(a, stream);
       }
     case 256:
