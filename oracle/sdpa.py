@@ -50,6 +50,8 @@ __all__ = [
     "decode",
     "merge_partials",
     "online_softmax_attention",
+    "attention_backward_rows",
+    "attention_backward",
 ]
 
 
@@ -245,3 +247,62 @@ def online_softmax_attention(q_rows, k_rows, v_rows, causal, scale, block_q, blo
             O[rows] = np.where(done[:, None], a / np.where(done, l, 1.0)[:, None], 0.0)
             LSE[rows] = np.where(done, m + np.log(np.where(done, l, 1.0)), -np.inf)
     return O, LSE
+
+
+def attention_backward_rows(q, k, v, do, causal, scale, b, hq):
+    """Gradients of one (batch, query head) block for an upstream gradient dO.
+
+    FlashAttention: Part 2, section 1.3: the backward pass keeps only the
+    row-wise log-sum-exp from the forward pass and recomputes the score
+    tiles (the pyshine.com code tour, on the kernel sources, describes the
+    same recompute-then-accumulate backward). What it computes is the
+    derivative of the forward definition (FlashAttention: Part 2, section
+    2.1, O = softmax(scale Q K^T) V), written out by the chain rule:
+
+        dV = P^T dO
+        dP = dO V^T
+        dS_ij = P_ij (dP_ij - sum_l P_il dP_il)      (softmax Jacobian)
+        dQ = scale dS K,   dK = scale dS^T Q
+
+    Returns (dq (Nq, d), dk (Nk, d), dv (Nk, dv)) for this query head; the
+    key/value gradients of a grouped head are the sums over its group.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    do = np.asarray(do)
+    _, Nq, Hq, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    kv = kv_head_of(hq, Hq, Hkv)
+    Q, K, V = _f64(q[b, :, hq, :]), _f64(k[b, :, kv, :]), _f64(v[b, :, kv, :])
+    dO = _f64(do[b, :, hq, :])
+    P, _ = softmax_rows(scores(Q, K, scale), visible_mask(Nq, Nk, causal))
+    dV = P.T @ dO
+    dP = dO @ V.T
+    dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+    dQ = float(scale) * (dS @ K)
+    dK = float(scale) * (dS.T @ Q)
+    return dQ, dK, dV
+
+
+def attention_backward(q, k, v, do, causal, scale):
+    """dq (B, Nq, Hq, d), dk and dv (B, Nk, Hkv, d) in float64.
+
+    Grouped query heads (pyshine.com code tour, "Why You Need This") read
+    the same key/value head, so that head's gradients sum over the group.
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    B, Nq, Hq, _ = q.shape
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(np.asarray(v).shape, dtype=np.float64)
+    Hkv = k.shape[2]
+    for b in range(B):
+        for hq in range(Hq):
+            kv = kv_head_of(hq, Hq, Hkv)
+            gq, gk, gv = attention_backward_rows(q, k, v, do, causal, scale, b, hq)
+            dq[b, :, hq, :] = gq
+            dk[b, :, kv, :] += gk
+            dv[b, :, kv, :] += gv
+    return dq, dk, dv

@@ -246,6 +246,72 @@ def pin_online_recurrence(tol=1e-12):
             assert np.max(np.abs(l - lb[0, 0])) <= tol, ("recurrence LSE", causal, bq, bk)
 
 
+# ---------------------------------------------------------------------------
+# backward pass
+# ---------------------------------------------------------------------------
+def _bwd_case(seed, B, Nq, Nk, Hq, Hkv, d):
+    q, k, v = rng_case(seed, B, Nq, Nk, Hq, Hkv, d)
+    do = np.random.default_rng(seed + 1).normal(size=q.shape[:3] + (v.shape[3],))
+    return q, k, v, do
+
+
+def pin_backward_torch_autograd(tol=1e-12):
+    """PyTorch CPU float64 autograd through scaled_dot_product_attention."""
+    import torch
+
+    q, k, v, do = _bwd_case(1500, 2, 7, 9, 4, 2, 5)
+    for causal in (False, True):
+        dq, dk, dv = O.attention_backward(q, k, v, do, causal, 0.6)
+        Q, K, V = (torch.tensor(x).permute(0, 2, 1, 3).requires_grad_() for x in (q, k, v))
+        o = torch.nn.functional.scaled_dot_product_attention(Q, K, V, is_causal=causal, scale=0.6,
+                                                             enable_gqa=True)
+        o.backward(torch.tensor(do).permute(0, 2, 1, 3))
+        for mine, ref, n in ((dq, Q.grad, "dq"), (dk, K.grad, "dk"), (dv, V.grad, "dv")):
+            assert np.max(np.abs(mine - ref.permute(0, 2, 1, 3).numpy())) <= tol, (n, causal)
+
+
+def pin_backward_finite_differences(tol=2e-7):
+    """Central differences of sum(O * dO) through the forward oracle."""
+    q, k, v, do = _bwd_case(1600, 1, 4, 5, 2, 1, 3)
+    h = 1e-5
+    for causal in (False, True):
+        grads = O.attention_backward(q, k, v, do, causal, 0.9)
+        for which, x in enumerate((q, k, v)):
+            for idx in [(0, 0, 0, 0), (0, 2, 0, 1), (0, 3, x.shape[2] - 1, 2)]:
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                args_p = [q, k, v]
+                args_m = [q, k, v]
+                args_p[which], args_m[which] = xp, xm
+                fp = np.sum(O.attention(*args_p, causal, 0.9)[0] * do)
+                fm = np.sum(O.attention(*args_m, causal, 0.9)[0] * do)
+                fd = (fp - fm) / (2 * h)
+                assert abs(fd - grads[which][idx]) <= tol, ("finite difference", which, idx, causal)
+
+
+def pin_backward_constant_values(tol=1e-13):
+    """Constant value rows make O independent of Q and K: dQ = dK = 0."""
+    q, k, v, do = _bwd_case(1700, 1, 6, 6, 2, 2, 4)
+    v[:] = v[:, :1]
+    for causal in (False, True):
+        dq, dk, dv = O.attention_backward(q, k, v, do, causal, 1.1)
+        assert np.max(np.abs(dq)) <= tol and np.max(np.abs(dk)) <= tol, ("constant V", causal)
+        # every query's weights sum to one, so the value gradients sum to dO
+        assert np.max(np.abs(dv.sum(axis=1) - do.reshape(1, 6, 2, 1, 4).sum(axis=(1, 3)))) <= 1e-12
+
+
+def pin_backward_gqa_sum(tol=1e-13):
+    """A grouped head's gradients are the sums over its repeated MHA heads."""
+    q, k, v, do = _bwd_case(1800, 1, 5, 5, 6, 2, 3)
+    for causal in (False, True):
+        dq, dk, dv = O.attention_backward(q, k, v, do, causal, 0.5)
+        dq2, dk2, dv2 = O.attention_backward(q, np.repeat(k, 3, axis=2), np.repeat(v, 3, axis=2), do, causal, 0.5)
+        assert np.max(np.abs(dq - dq2)) <= tol, "GQA dq"
+        assert np.max(np.abs(dk - dk2.reshape(1, 5, 2, 3, 3).sum(axis=3))) <= tol, "GQA dk"
+        assert np.max(np.abs(dv - dv2.reshape(1, 5, 2, 3, 3).sum(axis=3))) <= tol, "GQA dv"
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -262,4 +328,8 @@ ALL_PINS = [
     pin_split_combine,
     pin_decode,
     pin_online_recurrence,
+    pin_backward_torch_autograd,
+    pin_backward_finite_differences,
+    pin_backward_constant_values,
+    pin_backward_gqa_sum,
 ]

@@ -13,7 +13,7 @@ from oracle import sdpa as O
 
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
                                     "attention_rows", "decode", "merge_partials",
-                                    "online_softmax_attention")}
+                                    "online_softmax_attention", "attention_backward_rows")}
 
 
 def _interleaved_groups(hq, Hq, Hkv):
@@ -116,6 +116,31 @@ def _recurrence_wrong_alpha(q_rows, k_rows, v_rows, causal, scale, block_q, bloc
     return Oo, L
 
 
+def _bwd_variant(kind):
+    def f(q, k, v, do, causal, scale, b, hq):
+        q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+        _, Nq, Hq, _ = q.shape
+        Nk, Hkv = k.shape[1], k.shape[2]
+        kv = O.kv_head_of(hq, Hq, Hkv)
+        Q, K, V, dO = (np.asarray(x, float) for x in (q[b, :, hq], k[b, :, kv], v[b, :, kv], do[b, :, hq]))
+        P_, _ = O.softmax_rows(O.scores(Q, K, scale), O.visible_mask(Nq, Nk, causal))
+        dP = dO @ V.T
+        dS = P_ * (dP - np.sum(P_ * dP, axis=1, keepdims=True))
+        dQ, dK, dV = scale * (dS @ K), scale * (dS.T @ Q), P_.T @ dO
+        if kind == "no_softmax_correction":
+            dS = P_ * dP
+            dQ, dK = scale * (dS @ K), scale * (dS.T @ Q)
+        elif kind == "unscaled_dk":
+            dK = dS.T @ Q
+        elif kind == "dq_from_values":
+            dQ = scale * (dS @ V) if V.shape == K.shape else dQ * 2
+        elif kind == "dv_untransposed":
+            dV = (P_ @ dO[: P_.shape[1]]) if P_.shape[0] >= P_.shape[1] else np.zeros_like(dV)
+        return dQ, dK, dV
+    f.__name__ = "_bwd_" + kind
+    return f
+
+
 MUTATIONS = [
     ("kv_head_of", _interleaved_groups),
     ("visible_mask", _strict_causal),
@@ -131,6 +156,10 @@ MUTATIONS = [
     ("decode", _decode_off_by_one),
     ("merge_partials", _merge_plain_mean),
     ("online_softmax_attention", _recurrence_wrong_alpha),
+    ("attention_backward_rows", _bwd_variant("no_softmax_correction")),
+    ("attention_backward_rows", _bwd_variant("unscaled_dk")),
+    ("attention_backward_rows", _bwd_variant("dq_from_values")),
+    ("attention_backward_rows", _bwd_variant("dv_untransposed")),
 ]
 
 
