@@ -20,6 +20,8 @@ __all__ = [
     "fa_fwd_kvcache",
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
+    "fa_bwd",
+    "fa_bwd_workspace_size",
     "FA_DTYPE_BF16",
     "FA_DTYPE_F32",
 ]
@@ -60,6 +62,10 @@ def lib():
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
     L.fa_kvcache_default_splits.restype = i
     L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i]
+    L.fa_bwd_workspace_size.restype = sz
+    L.fa_bwd_workspace_size.argtypes = [i, i, i]
+    L.fa_bwd.restype = i
+    L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
     _lib = L
     return L
 
@@ -187,3 +193,50 @@ def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_split
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache")
     return o, lse
+
+
+def fa_bwd_workspace_size(B, Hq, Nq):
+    return int(lib().fa_bwd_workspace_size(int(B), int(Hq), int(Nq)))
+
+
+def fa_bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv=None, workspace=None,
+           stream=None):
+    """Attention backward through ``fa_bwd``.
+
+    q, o, dout: (B, Nq, Hq, d) bf16; k, v: (B, Nk, Hkv, d) bf16; lse:
+    (B, Hq, Nq) float32 from the forward. Gradient tensors and the
+    workspace are allocated when not given. Returns (dq, dk, dv).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be (batch, seq, heads, head_dim)")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Nk, Hkv, d) or tuple(v.shape) != (B, Nk, Hkv, d):
+        raise ValueError("k/v shapes do not match q")
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check(t, n, torch.bfloat16, q.device)
+    if tuple(o.shape) != tuple(q.shape) or tuple(dout.shape) != tuple(q.shape):
+        raise ValueError("o and dout must have q's shape")
+    _check(lse, "lse", torch.float32, q.device)
+    if tuple(lse.shape) != (B, Hq, Nq):
+        raise ValueError("lse must be (B, Hq, Nq)")
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n, ref in ((dq, "dq", q), (dk, "dk", k), (dv, "dv", v)):
+        _check(t, n, torch.bfloat16, q.device)
+        if tuple(t.shape) != tuple(ref.shape):
+            raise ValueError(f"{n} must have the shape of {n[1:]}")
+    need = fa_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                      B, Hq, Hkv, Nq, Nk, d, int(bool(causal)), float(scale), _ptr(workspace), ws_bytes,
+                      _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd")
+    return dq, dk, dv

@@ -140,4 +140,52 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
   return launch_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {
+  if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
+  return fa::bwd_workspace_bytes(B, Hq, Nq);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED;
+  // one-dimensional grids, and the workspace addressed with 32-bit offsets
+  const int64_t nq_pad = ((int64_t)Nq + 31) / 32 * 32;
+  if ((((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff || (((int64_t)Nk + 127) / 128) * Hkv * B > 0x7fffffff ||
+      2 * (int64_t)B * Hq * nq_pad * 4 > 0xffffffffLL || Hq > 65535 || B > 65535)
+    return FA_ERR_UNSUPPORTED;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
+  if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
+    return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return FA_ERR_INVALID_ARG;
+  const size_t need = Nq > 0 ? fa::bwd_workspace_bytes(B, Hq, Nq) : 0;
+  if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
+
+  fa::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.dout = dout;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  a.workspace = workspace;
+  return launch_status(fa::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,0 +1,569 @@
+// fa_bwd.hip - backward pass (dQ, dK, dV) in bf16 for gfx950.
+//
+// The backward keeps only the forward's row log-sum-exp and recomputes the
+// score tiles (FlashAttention: Part 2, section 1.3; the pyshine.com code
+// tour describes the same recompute-then-accumulate backward). With
+// P = exp(scale S - LSE) recomputed per tile, the gradients of
+// O = softmax(scale Q K^T) V are
+//     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),  D_i = sum_d dO_id O_id,
+//     dQ = scale dS K,  dK = scale dS^T Q,
+// where D_i equals sum_j P_ij dP_ij (FlashAttention: Part 2, section 1.3
+// credits FA2 with trimming such non-matmul work around the softmax).
+//
+// Three kernels, no atomics, so the result is bitwise reproducible:
+//  1. bwd_prep_kernel: D and -LSE/scale per (batch, head, query), into the
+//     caller's workspace (rows padded to a multiple of 32 queries, padded
+//     entries made inert: -LSE/scale = -inf gives P = 0).
+//  2. bwd_dq_kernel: one workgroup per 128-query tile of one head, the
+//     forward's layout (lane = query): S^T = K Q^T and dP^T = V dO^T from
+//     the same LDS K/V tiles, dQ^T += K^T dS^T.
+//  3. bwd_dkdv_kernel: one workgroup per 128-key tile of one key/value
+//     head, lane = key: it walks every query tile of every query head of
+//     the group, S = Q K^T and dP = dO V^T with K and V held in registers,
+//     dV^T += dO^T P and dK^T += Q^T dS, so a grouped head's gradients sum
+//     over its group inside the accumulators.
+#include <type_traits>
+
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+namespace {
+
+struct BwdParams {
+  const char* __restrict__ q;
+  const char* __restrict__ k;
+  const char* __restrict__ v;
+  const char* __restrict__ o;
+  const char* __restrict__ dout;
+  const float* __restrict__ lse;
+  char* __restrict__ dq;
+  char* __restrict__ dk;
+  char* __restrict__ dv;
+  float* __restrict__ dvec;  // D, (B, Hq, nq_pad)
+  float* __restrict__ nlse;  // -LSE / scale, (B, Hq, nq_pad)
+  int Nq, Nk, Hq, Hkv, group, B, causal;
+  int nq_pad;                // Nq rounded up to a multiple of 32
+  float c;                   // scale * log2(e)
+  float scale;
+};
+
+constexpr int kQStep = 32;  // queries per step of the dK/dV kernel (and the padding unit)
+
+// ---------------------------------------------------------------------------
+// 1. D = rowsum(dO o O) and -LSE/scale
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int TPR = D / 8;        // threads per (b, i, h) row, 8 elements each
+  constexpr int RPB = 256 / TPR;    // rows per workgroup
+  // rows are indexed over (b, h, i) with i running to the padded length
+  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int part = threadIdx.x % TPR;
+  const int64_t total = (int64_t)p.B * p.Hq * p.nq_pad;
+  float acc = 0.f;
+  int i = 0, h = 0, b = 0;
+  if (row < total) {
+    i = (int)(row % p.nq_pad);
+    const int64_t bh = row / p.nq_pad;
+    h = (int)(bh % p.Hq);
+    b = (int)(bh / p.Hq);
+    if (i < p.Nq) {
+      const int64_t off = (((int64_t)b * p.Nq + i) * p.Hq + h) * D * 2 + part * 16;
+      const bf16x8 x = *reinterpret_cast<const bf16x8*>(p.dout + off);
+      const bf16x8 y = *reinterpret_cast<const bf16x8*>(p.o + off);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    }
+  }
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w, 64);
+  if (row < total && part == 0) {
+    float nl = -INFINITY;  // padded rows: P = 0
+    if (i < p.Nq) {
+      const float l = p.lse[((int64_t)b * p.Hq + h) * p.Nq + i];
+      nl = l == -INFINITY ? -INFINITY : -l / p.scale;
+    }
+    p.dvec[row] = acc;
+    p.nlse[row] = nl;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 2. dQ: lane = query, the forward's tiling
+// ---------------------------------------------------------------------------
+template <int D_, int BN_>
+struct DqCfg {
+  static constexpr int D = D_, BN = BN_, NW = 4, BM = 128, THREADS = 256, NST = 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BN * D * 2;
+  static constexpr int V_REGION = NST * TILE;
+  static constexpr int DMA = TILE / (THREADS * 16);
+  static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0 && BN % 32 == 0, "dq tile");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int n_qtiles) {
+  constexpr int D = C::D, BN = C::BN, NST = C::NST, CPR = C::CPR, NBT = BN / 32;
+  __shared__ __attribute__((aligned(1024))) char smem[2 * NST * C::TILE];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+
+  // longest-first order over (query tile, head, batch), as the forward
+  const int heads = p.Hq * p.B;
+  const int r = blockIdx.x / heads;
+  const int rest = blockIdx.x - r * heads;
+  const int pairs = p.Hkv * p.B;
+  const int j = rest / pairs;
+  const int pr = rest - j * pairs;
+  const int b = pr / p.Hkv;
+  const int kvh = pr - b * p.Hkv;
+  const int hq = kvh * p.group + j;
+  const int qt = p.causal ? n_qtiles - 1 - r : r;
+  const int q0 = qt * C::BM;
+  const int qw0 = q0 + wave * 32;
+
+  const int64_t q_row = (int64_t)p.Hq * D * 2;
+  const int kv_row = p.Hkv * D * 2;
+  int kend = p.Nk;
+  if (p.causal) kend = min(kend, q0 + C::BM);
+  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+
+  const char* kbase = p.k + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  const char* vbase = p.v + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  int dma_row[C::DMA], dma_col[C::DMA];
+#pragma unroll
+  for (int jj = 0; jj < C::DMA; ++jj) {
+    const int slot = jj * C::THREADS + tid;
+    dma_row[jj] = slot / CPR;
+    dma_col[jj] = ((slot % CPR) ^ swz_pf<CPR>(slot / CPR)) * 16;
+  }
+  const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
+  auto issue_tile = [&](int t) __attribute__((always_inline)) {
+    const int j0 = t * BN;
+    const char* ks = kbase + (int64_t)j0 * kv_row;
+    const char* vs = vbase + (int64_t)j0 * kv_row;
+    const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::TILE);
+    const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
+#pragma unroll
+    for (int jj = 0; jj < C::DMA; ++jj) {
+      const uint32_t off = (uint32_t)(min(dma_row[jj], last) * kv_row + dma_col[jj]);
+      dma16(ks, off, st + jj * C::THREADS * 16);
+      dma16(vs, off, st + C::V_REGION + jj * C::THREADS * 16);
+    }
+  };
+  if (ntiles > 0) issue_tile(0);
+
+  // Q^T and dO^T as B operands: register i of k-step ks = X[row][16 ks + 8 g + i]
+  const int my_q = qw0 + r32;
+  bf16x8 qf[D / 16], of[D / 16];
+  {
+    const int64_t off = ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      qf[ks] = my_q < p.Nq ? *reinterpret_cast<const bf16x8*>(p.q + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      of[ks] = my_q < p.Nq ? *reinterpret_cast<const bf16x8*>(p.dout + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+    }
+  }
+  const int64_t vec = ((int64_t)b * p.Hq + hq) * p.nq_pad + min(my_q, p.nq_pad - 1);
+  const float cnl = p.c * p.nlse[vec];  // P = 2^(c s + cnl); -inf past Nq
+  const float dval = p.dvec[vec];
+  wait_vm_loads();
+
+  // LDS read offsets: K (and V) rows as A operands (b128), K^T through the
+  // transposing read, exactly as the forward reads K and V^T
+  uint32_t k_off[D / 16];
+  {
+    const int ksw = swz_pf<CPR>(r32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
+  }
+  uint32_t t_off[D / 32][2];
+  {
+    const int vi = lane & 15, vgrp = lane >> 4;
+    const int vcol = (vgrp & 1) * 2 + ((vi & 3) >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
+      const int sw = swz_pf<CPR>(row);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        t_off[dt][h] = (uint32_t)(row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
+    }
+  }
+
+  f32x16 acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
+
+  int nt_w = ntiles, nt_full = p.Nk / BN;
+  if (p.causal) {
+    nt_w = min(ntiles, (qw0 + 31) / BN + 1);
+    nt_full = min(nt_full, (qw0 + 1) / BN);
+  }
+  nt_full = min(nt_full, nt_w);
+
+  auto compute_tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const uint32_t ks_base = lds0 + (uint32_t)((t % NST) * C::TILE);
+    const uint32_t vs_base = ks_base + C::V_REGION;
+    f32x16 s[NBT], dp[NBT];
+#pragma unroll
+    for (int nb = 0; nb < NBT; ++nb) s[nb] = dp[nb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int nb = 0; nb < NBT; ++nb) {
+        const bf16x8 ka = *(const LDS3 bf16x8*)(uintptr_t)(ks_base + k_off[ks] + nb * 32 * D * 2);
+        const bf16x8 va = *(const LDS3 bf16x8*)(uintptr_t)(vs_base + k_off[ks] + nb * 32 * D * 2);
+        s[nb] = mfma32x32x16(ka, qf[ks], s[nb]);
+        dp[nb] = mfma32x32x16(va, of[ks], dp[nb]);
+      }
+    // dS^T = P^T o (dP^T - D), P^T = 2^(c s - c LSE / scale)
+    bf16x8 dsf[BN / 16];
+    const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - t * BN - 4 * g;
+#pragma unroll
+    for (int kk = 0; kk < BN / 16; ++kk) {
+      const int nb = kk >> 1, h = (kk & 1) * 8;
+      float e[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float pv = exp2_fast(fmaf(s[nb][h + i], p.c, cnl));
+        if constexpr (MASK) {
+          const int off = nb * 32 + 8 * ((h + i) >> 2) + ((h + i) & 3);
+          if (off > lim) pv = 0.f;
+        }
+        e[i] = pv * (dp[nb][h + i] - dval);
+      }
+      u32x4 w;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(e[2 * e2], e[2 * e2 + 1]);
+      dsf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < BN / 16; ++kk) {
+        const i16x4 v0 = ds_read_tr(ks_base + t_off[dt][0] + kk * 16 * D * 2);
+        const i16x4 v1 = ds_read_tr(ks_base + t_off[dt][1] + kk * 16 * D * 2);
+        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+        acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), dsf[kk], acc[dt]);
+      }
+  };
+
+  auto sync_tile = [&](int t) __attribute__((always_inline)) {
+    wait_vmcnt<0>();
+    barrier();  // everyone's loads of tile t landed; tile t-1 is no longer read
+    if (t + 1 < ntiles) issue_tile(t + 1);
+  };
+  int t = 0;
+  for (; t < nt_full; ++t) {
+    sync_tile(t);
+    compute_tile(t, std::false_type{});
+  }
+  for (; t < nt_w; ++t) {
+    sync_tile(t);
+    compute_tile(t, std::true_type{});
+  }
+  for (; t < ntiles; ++t) sync_tile(t);
+
+  if (my_q < p.Nq) {
+    char* row = p.dq + ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = dt * 32 + 8 * jj + 4 * g;
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[dt][4 * jj + 0] * p.scale, acc[dt][4 * jj + 1] * p.scale);
+        w[1] = pack_bf16x2(acc[dt][4 * jj + 2] * p.scale, acc[dt][4 * jj + 3] * p.scale);
+        *reinterpret_cast<u32x2*>(row + d0 * 2) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dK and dV: lane = key
+// ---------------------------------------------------------------------------
+template <int D_>
+struct DkvCfg {
+  static constexpr int D = D_, NW = 4, BK = 128, THREADS = 256, NST = 2, BQ = kQStep;
+  static constexpr int CPR = D / 8;
+  static constexpr int TILE = BQ * D * 2;                 // one Q (or dO) tile
+  static constexpr int DO_REGION = NST * TILE;
+  static constexpr int VEC_REGION = 2 * NST * TILE;       // per wave: 1 KiB per stage
+  static constexpr int LDS_BYTES = VEC_REGION + NST * NW * 1024;
+  static constexpr int DMA = TILE / (THREADS * 16);
+  static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0, "dkdv tile");
+};
+
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, int n_ktiles) {
+  constexpr int D = C::D, NST = C::NST, CPR = C::CPR, BQ = C::BQ;
+  __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int r32 = lane & 31;
+
+  // (key tile, key/value head, batch); with a causal mask the first key
+  // tiles see the most queries, so they go first
+  const int pairs = p.Hkv * p.B;
+  const int kt = blockIdx.x / pairs;
+  const int pr = blockIdx.x - kt * pairs;
+  const int b = pr / p.Hkv;
+  const int kvh = pr - b * p.Hkv;
+  const int k0 = kt * C::BK;
+  const int kw0 = k0 + wave * 32;     // first key of this wavefront
+  const int my_k = kw0 + r32;         // this lane's key (MFMA column)
+
+  const int kv_row = p.Hkv * D * 2;
+  const int64_t q_row = (int64_t)p.Hq * D * 2;
+
+  // K and V rows of this lane's key as B operands: register i of k-step ks
+  // = X[key][16 ks + 8 g + i]
+  bf16x8 kf[D / 16], vf[D / 16];
+  {
+    const int64_t off = ((int64_t)b * p.Nk + my_k) * kv_row + (int64_t)kvh * D * 2;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      kf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.k + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      vf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.v + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+    }
+  }
+
+  // steps: query tiles of BQ rows of each query head of the group; with a
+  // causal mask queries below this workgroup's first key see none of it
+  const int q_first = p.causal ? k0 / BQ : 0;
+  const int nqt = (p.Nq + BQ - 1) / BQ;
+  const int per_head = max(nqt - q_first, 0);
+  const int nsteps = k0 < p.Nk ? per_head * p.group : 0;
+
+  int dma_row[C::DMA], dma_col[C::DMA];
+#pragma unroll
+  for (int jj = 0; jj < C::DMA; ++jj) {
+    const int slot = jj * C::THREADS + tid;
+    dma_row[jj] = slot / CPR;
+    dma_col[jj] = ((slot % CPR) ^ swz_pf<CPR>(slot / CPR)) * 16;
+  }
+  const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
+  const uint32_t vec_lds = __builtin_amdgcn_readfirstlane(lds0 + C::VEC_REGION + wave * 1024);
+  const uint32_t nlse_gap = (uint32_t)((const char*)p.nlse - (const char*)p.dvec);
+  auto step_head = [&](int s) __attribute__((always_inline)) { return kvh * p.group + s / per_head; };
+  auto step_q0 = [&](int s) __attribute__((always_inline)) { return (q_first + s % per_head) * BQ; };
+  auto issue_step = [&](int s) __attribute__((always_inline)) {
+    const int hq = step_head(s), q0 = step_q0(s);
+    const char* qs = p.q + ((int64_t)b * p.Nq + q0) * q_row + (int64_t)hq * D * 2;
+    const char* os = p.dout + ((int64_t)b * p.Nq + q0) * q_row + (int64_t)hq * D * 2;
+    const uint32_t st = dma_lds + (uint32_t)((s % NST) * C::TILE);
+    const int last = p.Nq - 1 - q0;  // rows past the end re-read the last query (P = 0 there)
+#pragma unroll
+    for (int jj = 0; jj < C::DMA; ++jj) {
+      const uint32_t off = (uint32_t)(min(dma_row[jj], last) * (int)q_row + dma_col[jj]);
+      dma16(qs, off, st + jj * C::THREADS * 16);
+      dma16(os, off, st + C::DO_REGION + jj * C::THREADS * 16);
+    }
+    // -LSE/scale (lanes 0-7) and D (lanes 8-15) of the step's 32 queries,
+    // padded rows included; the other lanes repeat them. The base is the D
+    // row; the -LSE/scale row sits nlse_gap bytes after it.
+    const int vl = lane & 15;
+    const uint32_t voff = (vl < 8 ? nlse_gap : 0u) + 16u * (uint32_t)(vl & 7);
+    dma16(p.dvec + ((int64_t)b * p.Hq + hq) * p.nq_pad + q0, voff,
+          vec_lds + (uint32_t)((s % NST) * (C::NW * 1024)));
+  };
+  if (nsteps > 0) issue_step(0);
+  wait_vm_loads();
+
+  // LDS read offsets: Q and dO rows as A operands (b128), Q^T and dO^T
+  // through the transposing read
+  uint32_t a_off[D / 16];
+  {
+    const int ksw = swz_pf<CPR>(r32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) a_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
+  }
+  uint32_t t_off[D / 32][2];
+  {
+    const int vi = lane & 15, vgrp = lane >> 4;
+    const int vcol = (vgrp & 1) * 2 + ((vi & 3) >> 1);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
+      const int sw = swz_pf<CPR>(row);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        t_off[dt][h] = (uint32_t)(row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
+    }
+  }
+
+  f32x16 acck[D / 32], accv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acck[dt] = accv[dt] = f32x16{};
+
+  auto compute_step = [&](int s, auto mask_tag) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    const int q0 = step_q0(s);
+    const uint32_t qs = lds0 + (uint32_t)((s % NST) * C::TILE);
+    const uint32_t os = qs + C::DO_REGION;
+    const uint32_t vs = vec_lds + (uint32_t)((s % NST) * (C::NW * 1024));
+    // accumulator register i holds query m = 8 (i / 4) + 4 g + i % 4 of the step
+    f32x16 sacc, dpacc;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const f32x4 nl = *(const LDS3 f32x4*)(uintptr_t)(vs + (8 * q4 + 4 * g) * 4);
+      const f32x4 dd = *(const LDS3 f32x4*)(uintptr_t)(vs + 128 + (8 * q4 + 4 * g) * 4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        sacc[4 * q4 + e] = nl[e];    // S - LSE / scale after the products
+        dpacc[4 * q4 + e] = -dd[e];  // dP - D after the products
+      }
+    }
+    // S = Q K^T and dP = dO V^T, query x key
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 qa = *(const LDS3 bf16x8*)(uintptr_t)(qs + a_off[ks]);
+      const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks]);
+      sacc = mfma32x32x16(qa, kf[ks], sacc);
+      dpacc = mfma32x32x16(oa, vf[ks], dpacc);
+    }
+    // P and dS = P o (dP - D), packed as B operands over the query index
+    bf16x8 pf[BQ / 16], sf[BQ / 16];
+#pragma unroll
+    for (int kk = 0; kk < BQ / 16; ++kk) {
+      const int h = (kk & 1) * 8;
+      float pe[8], se[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float pv = exp2_fast(sacc[h + i] * p.c);
+        if constexpr (MASK) {
+          const int qm = q0 + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
+          if (my_k > qm) pv = 0.f;  // causal: key j visible to query i iff j <= i
+        }
+        pe[i] = pv;
+        se[i] = pv * dpacc[h + i];
+      }
+      u32x4 wp, ws;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        wp[e2] = pack_bf16x2(pe[2 * e2], pe[2 * e2 + 1]);
+        ws[e2] = pack_bf16x2(se[2 * e2], se[2 * e2 + 1]);
+      }
+      pf[kk] = __builtin_bit_cast(bf16x8, wp);
+      sf[kk] = __builtin_bit_cast(bf16x8, ws);
+    }
+    // dV^T += dO^T P and dK^T += Q^T dS, d x key
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < BQ / 16; ++kk) {
+        const i16x4 o0 = ds_read_tr(os + t_off[dt][0] + kk * 16 * D * 2);
+        const i16x4 o1 = ds_read_tr(os + t_off[dt][1] + kk * 16 * D * 2);
+        const i16x8 ov = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+        accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), pf[kk], accv[dt]);
+        const i16x4 q0v = ds_read_tr(qs + t_off[dt][0] + kk * 16 * D * 2);
+        const i16x4 q1v = ds_read_tr(qs + t_off[dt][1] + kk * 16 * D * 2);
+        const i16x8 qv = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+        acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), sf[kk], acck[dt]);
+      }
+  };
+
+  for (int s = 0; s < nsteps; ++s) {
+    wait_vmcnt<0>();
+    barrier();  // everyone's loads of step s landed; step s-1 is no longer read
+    if (s + 1 < nsteps) issue_step(s + 1);
+    // a step needs the causal mask when some of its queries precede some of
+    // this wavefront's keys
+    const int q0 = step_q0(s);
+    if (p.causal && q0 < kw0 + 31) compute_step(s, std::true_type{});
+    else compute_step(s, std::false_type{});
+  }
+
+  if (my_k < p.Nk) {
+    const int64_t off = ((int64_t)b * p.Nk + my_k) * kv_row + (int64_t)kvh * D * 2;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = dt * 32 + 8 * jj + 4 * g;
+        u32x2 wk, wv;
+        wk[0] = pack_bf16x2(acck[dt][4 * jj + 0] * p.scale, acck[dt][4 * jj + 1] * p.scale);
+        wk[1] = pack_bf16x2(acck[dt][4 * jj + 2] * p.scale, acck[dt][4 * jj + 3] * p.scale);
+        wv[0] = pack_bf16x2(accv[dt][4 * jj + 0], accv[dt][4 * jj + 1]);
+        wv[1] = pack_bf16x2(accv[dt][4 * jj + 2], accv[dt][4 * jj + 3]);
+        *reinterpret_cast<u32x2*>(p.dk + off + d0 * 2) = wk;
+        *reinterpret_cast<u32x2*>(p.dv + off + d0 * 2) = wv;
+      }
+  }
+}
+
+template <int D>
+hipError_t launch(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const char*>(a.q);
+  p.k = static_cast<const char*>(a.k);
+  p.v = static_cast<const char*>(a.v);
+  p.o = static_cast<const char*>(a.o);
+  p.dout = static_cast<const char*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<char*>(a.dq);
+  p.dk = static_cast<char*>(a.dk);
+  p.dv = static_cast<char*>(a.dv);
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.B = a.B;
+  p.causal = a.causal;
+  p.nq_pad = (a.Nq + kQStep - 1) / kQStep * kQStep;
+  p.c = a.scale * kLog2e;
+  p.scale = a.scale;
+  p.dvec = static_cast<float*>(a.workspace);
+  p.nlse = p.dvec + (size_t)a.B * a.Hq * p.nq_pad;
+
+  const int64_t rows = (int64_t)a.B * a.Hq * p.nq_pad;
+  if (rows > 0) {
+    constexpr int RPB = 256 / (D / 8);
+    hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
+  }
+  using QC = DqCfg<D, 32>;
+  const int n_qtiles = (a.Nq + QC::BM - 1) / QC::BM;
+  if (n_qtiles > 0) {
+    hipLaunchKernelGGL((bwd_dq_kernel<QC>), dim3(n_qtiles * a.Hq * a.B), dim3(QC::THREADS), 0, stream, p, n_qtiles);
+  }
+  using KC = DkvCfg<D>;
+  const int n_ktiles = (a.Nk + KC::BK - 1) / KC::BK;
+  if (n_ktiles > 0) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<KC>), dim3(n_ktiles * a.Hkv * a.B), dim3(KC::THREADS), 0, stream, p,
+                       n_ktiles);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_supported(int d) { return d == 64 || d == 128; }
+
+size_t bwd_workspace_bytes(int B, int Hq, int Nq) {
+  const size_t pad = ((size_t)Nq + kQStep - 1) / kQStep * kQStep;
+  return 2 * (size_t)B * Hq * pad * sizeof(float);
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  switch (a.d) {
+    case 64: return launch<64>(a, stream);
+    case 128: return launch<128>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace fa

@@ -35,6 +35,22 @@ struct DecodeArgs {
   void* workspace;  // >= decode_workspace_bytes(...) when num_splits > 1
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Nq, Nk, d;
+  int causal;
+  float scale;
+  void* workspace;  // >= bwd_workspace_bytes(B, Hq, Nq)
+};
+
 // Keys per split for a cache of `capacity` rows cut into `num_splits`
 // pieces: the smallest multiple of the decode key tile >= ceil(cap / S).
 int decode_chunk(int capacity, int num_splits);
@@ -43,9 +59,12 @@ size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits);
 bool fwd_bf16_supported(int d);
 bool fwd_f32_supported(int d);
 bool decode_supported(int d, int group);
+bool bwd_supported(int d);
+size_t bwd_workspace_bytes(int B, int Hq, int Nq);
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 }  // namespace fa

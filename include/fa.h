@@ -132,6 +132,38 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
  * per resident slot. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);
 
+/* Bytes of device workspace fa_bwd needs: two float32 values (D_i and
+ * -LSE_i / scale) per (batch, query head, query), the query count rounded
+ * up to a multiple of 32. 0 when B, Hq or Nq is not positive. */
+size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
+
+/* Attention backward: dQ, dK, dV of O = softmax(scale * Q K^T) V for an
+ * upstream gradient dO, from the forward's O and LSE (the score tiles are
+ * recomputed from the saved row log-sum-exp, never stored: FlashAttention:
+ * Part 2, section 1.3; the pyshine.com code tour's "recompute then
+ * accumulate" backward). With P = exp(scale S - LSE):
+ *     dV = P^T dO, dP = dO V^T, dS = P o (dP - D), D_i = sum_d dO_id O_id,
+ *     dQ = scale dS K, dK = scale dS^T Q;
+ * a key/value head's gradients are summed over its group of query heads.
+ *
+ *   q, o, dout, dq : (B, Nq, Hq, d) bfloat16      lse : (B, Hq, Nq) float32,
+ *   k, v, dk, dv   : (B, Nk, Hkv, d) bfloat16     as fa_fwd writes it
+ *   causal, scale  : as fa_fwd (top-left mask, finite positive scale)
+ *   workspace      : device memory of at least fa_bwd_workspace_size(B, Hq, Nq)
+ *                    bytes (may be NULL when that is 0); contents need no
+ *                    initialisation and are overwritten.
+ *
+ * dq, dk, dv are fully overwritten (rows with no visible key get zeros);
+ * nothing is accumulated into them, and no atomics are used, so results
+ * are bitwise reproducible.
+ * Returns FA_ERR_INVALID_ARG (as fa_fwd), FA_ERR_UNSUPPORTED for d other
+ * than 64 or 128 or for grids/workspaces beyond 32-bit indexing,
+ * FA_ERR_WORKSPACE when the workspace is missing or too small. */
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
