@@ -111,6 +111,8 @@ def main():
     ap.add_argument("--splits", type=int, default=0, help="decode num_splits (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--bwd-steps", type=int, default=50,
+                    help="timed fa_bwd calls on the prefill workload after the step loop (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (outside the timed "
                          "region) as the known-size reference for HBM byte counters")
@@ -187,6 +189,38 @@ def main():
     tflops = flops / (pf_mean * 1e-3) / 1e12
     gbs = dec_bytes / (dc_mean * 1e-3) / 1e9
 
+    # The backward of the same prefill workload (fa_bwd: dQ, dK, dV from the
+    # forward's O and LSE), timed after the step loop. Algorithmic work: the
+    # five N x N x d products of the gradient formulas, 2.5x the forward's.
+    bwd = None
+    if args.bwd_steps > 0 and wp["dtype"] == "bf16" and wp["d"] in (64, 128):
+        g = torch.Generator(device=dev)
+        g.manual_seed(wp["seed"] + 1000)
+        dout = torch.randn(q.shape, generator=g, device=dev).to(q.dtype)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        bws = torch.empty(max(fa.fa_bwd_workspace_size(wp["B"], wp["Hq"], wp["Nq"]), 1), dtype=torch.uint8,
+                          device=dev)
+        fa.fa_fwd(q, k, v, o=o, lse=lse, causal=wp["causal"], scale=scale_p)
+
+        def bstep():
+            fa.fa_bwd(q, k, v, o, lse, dout, causal=wp["causal"], scale=scale_p, dq=dq, dk=dk, dv=dv,
+                      workspace=bws)
+        for _ in range(max(3, args.bwd_steps // 5)):
+            bstep()
+        torch.cuda.synchronize()
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.bwd_steps)]
+        for e0, e1 in bev:
+            e0.record()
+            bstep()
+            e1.record()
+        torch.cuda.synchronize()
+        b_ms = sum(e0.elapsed_time(e1) for e0, e1 in bev) / len(bev)
+        b_tf = 2.5 * prefill_flops(wp) / (b_ms * 1e-3) / 1e12
+        bwd = {"value": round(b_tf, 2), "unit": "TFLOP/s", "mean_launch_ms": round(b_ms, 5),
+               "frac": round(b_tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_launch": 2.5 * prefill_flops(wp),
+               "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "steps": args.bwd_steps}
+
     traffic = stored_traffic("prefill:" + args.prefill, PREFILL_KERNEL_SOURCE)
     dec_traffic = stored_traffic("decode:" + args.decode, DECODE_KERNEL_SOURCE)
 
@@ -228,6 +262,7 @@ def main():
                          "algorithmic_bytes_per_launch": dec_bytes, "mean_launch_ms": round(dc_mean, 5)},
             "num_splits": S,
         },
+        "backward": bwd,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }
