@@ -22,6 +22,8 @@
 //     the group, S = Q K^T and dP = dO V^T with K and V held in registers,
 //     dV^T += dO^T P and dK^T += Q^T dS, so a grouped head's gradients sum
 //     over its group inside the accumulators.
+#include <stdlib.h>
+
 #include <type_traits>
 
 #include "fa_device.h"
@@ -303,8 +305,15 @@ struct DkvCfg {
   static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0, "dkdv tile");
 };
 
-template <class C>
-__global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, int n_ktiles) {
+// WHAT selects the gradients a launch produces: kDV (S, P, dV^T += dO^T P),
+// kDK (S, P, dP, dS, dK^T += Q^T dS) or both in one pass (the default: the
+// split pair recomputes S once more, and although its dV half runs two
+// wavefronts per SIMD, the pair measured slower than the single pass).
+constexpr int kDV = 1, kDK = 2, kDKDV = 3;
+
+template <class C, int WHAT, int WPS>
+__global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, int n_ktiles) {
+  constexpr bool DV = (WHAT & kDV) != 0, DK = (WHAT & kDK) != 0;
   constexpr int D = C::D, NST = C::NST, CPR = C::CPR, BQ = C::BQ;
   __shared__ __attribute__((aligned(1024))) char smem[C::LDS_BYTES];
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
@@ -337,7 +346,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, in
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       kf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.k + off + (ks * 16 + g * 8) * 2) : bf16x8{};
-      vf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.v + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      if constexpr (DK)
+        vf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.v + off + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
 
@@ -431,9 +441,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, in
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
       const bf16x8 qa = *(const LDS3 bf16x8*)(uintptr_t)(qs + a_off[ks]);
-      const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks]);
       sacc = mfma32x32x16(qa, kf[ks], sacc);
-      dpacc = mfma32x32x16(oa, vf[ks], dpacc);
+      if constexpr (DK) {
+        const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks]);
+        dpacc = mfma32x32x16(oa, vf[ks], dpacc);
+      }
     }
     // P and dS = P o (dP - D), packed as B operands over the query index
     bf16x8 pf[BQ / 16], sf[BQ / 16];
@@ -465,14 +477,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, in
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int kk = 0; kk < BQ / 16; ++kk) {
-        const i16x4 o0 = ds_read_tr(os + t_off[dt][0] + kk * 16 * D * 2);
-        const i16x4 o1 = ds_read_tr(os + t_off[dt][1] + kk * 16 * D * 2);
-        const i16x8 ov = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-        accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), pf[kk], accv[dt]);
-        const i16x4 q0v = ds_read_tr(qs + t_off[dt][0] + kk * 16 * D * 2);
-        const i16x4 q1v = ds_read_tr(qs + t_off[dt][1] + kk * 16 * D * 2);
-        const i16x8 qv = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-        acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), sf[kk], acck[dt]);
+        if constexpr (DV) {
+          const i16x4 o0 = ds_read_tr(os + t_off[dt][0] + kk * 16 * D * 2);
+          const i16x4 o1 = ds_read_tr(os + t_off[dt][1] + kk * 16 * D * 2);
+          const i16x8 ov = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
+          accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), pf[kk], accv[dt]);
+        }
+        if constexpr (DK) {
+          const i16x4 q0v = ds_read_tr(qs + t_off[dt][0] + kk * 16 * D * 2);
+          const i16x4 q1v = ds_read_tr(qs + t_off[dt][1] + kk * 16 * D * 2);
+          const i16x8 qv = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
+          acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), sf[kk], acck[dt]);
+        }
       }
   };
 
@@ -499,10 +515,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void bwd_dkdv_kernel(BwdParams p, in
         wk[1] = pack_bf16x2(acck[dt][4 * jj + 2] * p.scale, acck[dt][4 * jj + 3] * p.scale);
         wv[0] = pack_bf16x2(accv[dt][4 * jj + 0], accv[dt][4 * jj + 1]);
         wv[1] = pack_bf16x2(accv[dt][4 * jj + 2], accv[dt][4 * jj + 3]);
-        *reinterpret_cast<u32x2*>(p.dk + off + d0 * 2) = wk;
-        *reinterpret_cast<u32x2*>(p.dv + off + d0 * 2) = wv;
+        if constexpr (DK) *reinterpret_cast<u32x2*>(p.dk + off + d0 * 2) = wk;
+        if constexpr (DV) *reinterpret_cast<u32x2*>(p.dv + off + d0 * 2) = wv;
       }
   }
+}
+
+// Kernel-shape override for tuning (FA_BWD_VARIANT), read once per process.
+int bwd_variant() {
+  static const int v = [] {
+    const char* e = getenv("FA_BWD_VARIANT");
+    return e ? atoi(e) : 0;
+  }();
+  return v;
 }
 
 template <int D>
@@ -543,8 +568,13 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using KC = DkvCfg<D>;
   const int n_ktiles = (a.Nk + KC::BK - 1) / KC::BK;
   if (n_ktiles > 0) {
-    hipLaunchKernelGGL((bwd_dkdv_kernel<KC>), dim3(n_ktiles * a.Hkv * a.B), dim3(KC::THREADS), 0, stream, p,
-                       n_ktiles);
+    const dim3 grid(n_ktiles * a.Hkv * a.B);
+    if (bwd_variant() == 1) {  // split pair: measured 9-15% slower on MI355X
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+    } else {
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+    }
   }
   return hipGetLastError();
 }
