@@ -20,6 +20,7 @@ __all__ = [
     "fa_fwd_kvcache",
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
+    "fa_fwd_kvcache_paged",
     "fa_bwd",
     "fa_bwd_workspace_size",
     "FA_DTYPE_BF16",
@@ -62,6 +63,8 @@ def lib():
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
     L.fa_kvcache_default_splits.restype = i
     L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i]
+    L.fa_fwd_kvcache_paged.restype = i
+    L.fa_fwd_kvcache_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd_workspace_size.argtypes = [i, i, i]
     L.fa_bwd.restype = i
@@ -192,6 +195,51 @@ def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_split
                               _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache")
+    return o, lse
+
+
+def fa_fwd_kvcache_paged(q, kpages, vpages, block_table, cache_seqlens, o=None, lse=None, num_splits=None,
+                         scale=None, workspace=None, stream=None, want_lse=True):
+    """Split-KV decode over a paged cache through ``fa_fwd_kvcache_paged``.
+
+    q: (B, 1, Hq, d) bf16; kpages, vpages: (num_pages, page_size, Hkv, d)
+    bf16; block_table: (B, pages_per_seq) int32; cache_seqlens: (B,) int32,
+    all on one GPU. Returns (o (B, 1, Hq, d) bf16, lse (B, Hq) float32).
+    """
+    import torch
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be (batch, 1, heads, head_dim)")
+    B, _, Hq, d = q.shape
+    num_pages, page_size, Hkv, dk = kpages.shape
+    if dk != d or tuple(vpages.shape) != tuple(kpages.shape):
+        raise ValueError("page pool shapes do not match q")
+    for t, n in ((q, "q"), (kpages, "kpages"), (vpages, "vpages")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(block_table, "block_table", torch.int32, q.device)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != B or tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("block_table must be (B, pages_per_seq) and cache_seqlens (B,)")
+    pages_per_seq = block_table.shape[1]
+    if num_splits is None:
+        num_splits = fa_kvcache_default_splits(B, Hkv, page_size * pages_per_seq)
+    if o is None:
+        o = torch.empty_like(q)
+    _check(o, "o", torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+    need = fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_kvcache_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(block_table), _ptr(cache_seqlens),
+                                    _ptr(o), _ptr(lse), int(num_splits), B, Hq, Hkv, page_size, pages_per_seq,
+                                    num_pages, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache_paged")
     return o, lse
 
 

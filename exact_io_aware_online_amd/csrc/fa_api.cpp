@@ -107,10 +107,13 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs
   return (int)s;
 }
 
-fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache,
-                           const int32_t* cache_seqlens, void* o, float* lse,
-                           int num_splits, int B, int Hq, int Hkv, int capacity, int d,
-                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+namespace {
+
+fa_status_t kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
+                    int page_size, int pages_per_seq, int num_pages,
+                    const int32_t* cache_seqlens, void* o, float* lse,
+                    int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
@@ -137,7 +140,34 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
   a.d = d;
   a.scale = scale;
   a.workspace = workspace;
+  a.block_table = block_table;
+  a.page_size = page_size;
+  a.pages_per_seq = pages_per_seq;
+  a.num_pages = num_pages;
   return launch_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache,
+                           const int32_t* cache_seqlens, void* o, float* lse,
+                           int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                           float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return kvcache(q, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, num_splits, B, Hq, Hkv, capacity, d,
+                 scale, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* vpages,
+                                 const int32_t* block_table, const int32_t* cache_seqlens, void* o, float* lse,
+                                 int num_splits, int B, int Hq, int Hkv, int page_size, int pages_per_seq,
+                                 int num_pages, int d, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (page_size <= 0 || page_size % fa::kDecodePageAlign != 0 || pages_per_seq <= 0 || num_pages <= 0)
+    return FA_ERR_INVALID_ARG;
+  if ((int64_t)page_size * pages_per_seq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && block_table == nullptr) return FA_ERR_INVALID_ARG;
+  return kvcache(q, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens, o, lse,
+                 num_splits, B, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace, workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {

@@ -45,12 +45,14 @@ struct BwdParams {
   float* __restrict__ dvec;  // D, (B, Hq, nq_pad)
   float* __restrict__ nlse;  // -LSE / scale, (B, Hq, nq_pad)
   int Nq, Nk, Hq, Hkv, group, B, causal;
-  int nq_pad;                // Nq rounded up to a multiple of 32
+  int nq_pad;                // Nq rounded up to a multiple of kQStep
   float c;                   // scale * log2(e)
   float scale;
 };
 
-constexpr int kQStep = 32;  // queries per step of the dK/dV kernel (and the padding unit)
+// queries per step of the dK/dV kernel (and the padding unit); 64 was
+// measured to spill the single-pass kernel's 512 registers per lane
+constexpr int kQStep = 32;
 
 // ---------------------------------------------------------------------------
 // 1. D = rowsum(dO o O) and -LSE/scale
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
 // ---------------------------------------------------------------------------
 template <int D_>
 struct DkvCfg {
-  static constexpr int D = D_, NW = 4, BK = 128, THREADS = 256, NST = 2, BQ = kQStep;
+  static constexpr int D = D_, NW = 4, BK = 128, THREADS = 256, NST = 2, BQ = kQStep, NQB = BQ / 32;
   static constexpr int CPR = D / 8;
   static constexpr int TILE = BQ * D * 2;                 // one Q (or dO) tile
   static constexpr int DO_REGION = NST * TILE;
@@ -382,11 +384,11 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
       dma16(qs, off, st + jj * C::THREADS * 16);
       dma16(os, off, st + C::DO_REGION + jj * C::THREADS * 16);
     }
-    // -LSE/scale (lanes 0-7) and D (lanes 8-15) of the step's 32 queries,
-    // padded rows included; the other lanes repeat them. The base is the D
-    // row; the -LSE/scale row sits nlse_gap bytes after it.
-    const int vl = lane & 15;
-    const uint32_t voff = (vl < 8 ? nlse_gap : 0u) + 16u * (uint32_t)(vl & 7);
+    // -LSE/scale (lanes 0 .. BQ/4-1) and D (the next BQ/4 lanes) of the
+    // step's queries, padded rows included; the other lanes repeat them.
+    // The base is the D row; the -LSE/scale row sits nlse_gap bytes after it.
+    const int vl = lane & (BQ / 2 - 1);
+    const uint32_t voff = (vl < BQ / 4 ? nlse_gap : 0u) + 16u * (uint32_t)(vl & (BQ / 4 - 1));
     dma16(p.dvec + ((int64_t)b * p.Hq + hq) * p.nq_pad + q0, voff,
           vec_lds + (uint32_t)((s % NST) * (C::NW * 1024)));
   };
@@ -425,43 +427,48 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
     const uint32_t qs = lds0 + (uint32_t)((s % NST) * C::TILE);
     const uint32_t os = qs + C::DO_REGION;
     const uint32_t vs = vec_lds + (uint32_t)((s % NST) * (C::NW * 1024));
-    // accumulator register i holds query m = 8 (i / 4) + 4 g + i % 4 of the step
-    f32x16 sacc, dpacc;
+    // accumulator register i of query block qb holds query
+    // m = 32 qb + 8 (i / 4) + 4 g + i % 4 of the step
+    f32x16 sacc[C::NQB], dpacc[C::NQB];
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const f32x4 nl = *(const LDS3 f32x4*)(uintptr_t)(vs + (8 * q4 + 4 * g) * 4);
-      const f32x4 dd = *(const LDS3 f32x4*)(uintptr_t)(vs + 128 + (8 * q4 + 4 * g) * 4);
+    for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        sacc[4 * q4 + e] = nl[e];    // S - LSE / scale after the products
-        dpacc[4 * q4 + e] = -dd[e];  // dP - D after the products
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 nl = *(const LDS3 f32x4*)(uintptr_t)(vs + (32 * qb + 8 * q4 + 4 * g) * 4);
+        const f32x4 dd = *(const LDS3 f32x4*)(uintptr_t)(vs + BQ * 4 + (32 * qb + 8 * q4 + 4 * g) * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          sacc[qb][4 * q4 + e] = nl[e];    // S - LSE / scale after the products
+          dpacc[qb][4 * q4 + e] = -dd[e];  // dP - D after the products
+        }
       }
-    }
     // S = Q K^T and dP = dO V^T, query x key
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 qa = *(const LDS3 bf16x8*)(uintptr_t)(qs + a_off[ks]);
-      sacc = mfma32x32x16(qa, kf[ks], sacc);
-      if constexpr (DK) {
-        const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks]);
-        dpacc = mfma32x32x16(oa, vf[ks], dpacc);
+    for (int ks = 0; ks < D / 16; ++ks)
+#pragma unroll
+      for (int qb = 0; qb < C::NQB; ++qb) {
+        const bf16x8 qa = *(const LDS3 bf16x8*)(uintptr_t)(qs + a_off[ks] + qb * 32 * D * 2);
+        sacc[qb] = mfma32x32x16(qa, kf[ks], sacc[qb]);
+        if constexpr (DK) {
+          const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks] + qb * 32 * D * 2);
+          dpacc[qb] = mfma32x32x16(oa, vf[ks], dpacc[qb]);
+        }
       }
-    }
     // P and dS = P o (dP - D), packed as B operands over the query index
     bf16x8 pf[BQ / 16], sf[BQ / 16];
 #pragma unroll
     for (int kk = 0; kk < BQ / 16; ++kk) {
-      const int h = (kk & 1) * 8;
+      const int qb = kk >> 1, h = (kk & 1) * 8;
       float pe[8], se[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        float pv = exp2_fast(sacc[h + i] * p.c);
+        float pv = exp2_fast(sacc[qb][h + i] * p.c);
         if constexpr (MASK) {
-          const int qm = q0 + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
+          const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
           if (my_k > qm) pv = 0.f;  // causal: key j visible to query i iff j <= i
         }
         pe[i] = pv;
-        se[i] = pv * dpacc[h + i];
+        se[i] = pv * dpacc[qb][h + i];
       }
       u32x4 wp, ws;
 #pragma unroll

@@ -46,6 +46,11 @@ struct DecParams {
   float* __restrict__ part_lse;  // (B, Hq, S), base-2 units
   int Hq, Hkv, group, capacity, S, chunk;
   float c;  // scale * log2(e)
+  // paged cache (block_table non-null): sequence b's keys [i P, (i+1) P)
+  // sit in page block_table[b * pages_per_seq + i] of kc / vc, each page
+  // P = page_size rows of (Hkv, D); indices are clamped to [0, num_pages)
+  const int32_t* __restrict__ block_table;
+  int page_size, pages_per_seq, num_pages;
 };
 
 __device__ __forceinline__ int seq_len(const DecParams& p, int b) {
@@ -108,6 +113,16 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
     const int last = end - start - 1 - j0;  // rows past the end re-read the last key (masked later)
     const char* ks = kbase + (int64_t)j0 * kv_row;
     const char* vs = vbase + (int64_t)j0 * kv_row;
+    if (p.block_table != nullptr) {
+      // a tile never straddles pages: page_size and the split starts are
+      // multiples of the 64-key split alignment, tiles divide it
+      const int key = start + j0;
+      const int slot = key / p.page_size;
+      const int page = min(max(p.block_table[(int64_t)b * p.pages_per_seq + slot], 0), p.num_pages - 1);
+      const int64_t row = (int64_t)page * p.page_size + (key - slot * p.page_size);
+      ks = p.kc + (row * p.Hkv + h) * D * 2;
+      vs = p.vc + (row * p.Hkv + h) * D * 2;
+    }
     const uint32_t st = lds0 + (uint32_t)((t % NST) * TL::STAGE);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
@@ -320,6 +335,10 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.c = a.scale * kLog2e;
   p.part_o = nullptr;
   p.part_lse = nullptr;
+  p.block_table = a.block_table;
+  p.page_size = a.page_size;
+  p.pages_per_seq = a.pages_per_seq;
+  p.num_pages = a.num_pages;
   if (p.S > 1) {
     p.part_o = static_cast<float*>(a.workspace);
     p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;

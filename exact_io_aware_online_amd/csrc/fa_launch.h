@@ -33,6 +33,9 @@ struct DecodeArgs {
   int B, Hq, Hkv, capacity, d;
   float scale;
   void* workspace;  // >= decode_workspace_bytes(...) when num_splits > 1
+  // paged cache: null for a contiguous (B, capacity, Hkv, d) cache
+  const int32_t* block_table = nullptr;
+  int page_size = 0, pages_per_seq = 0, num_pages = 0;
 };
 
 struct BwdArgs {
@@ -54,6 +57,7 @@ struct BwdArgs {
 // Keys per split for a cache of `capacity` rows cut into `num_splits`
 // pieces: the smallest multiple of the decode key tile >= ceil(cap / S).
 int decode_chunk(int capacity, int num_splits);
+constexpr int kDecodePageAlign = 64;  // page sizes must be multiples of this
 size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits);
 
 bool fwd_bf16_supported(int d);

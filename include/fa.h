@@ -132,6 +132,25 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
  * per resident slot. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);
 
+/* fa_fwd_kvcache over a paged cache (pyshine.com FlashAttention code tour:
+ * the paged KV cache of flash_attn_with_kvcache, after the PagedAttention
+ * layout). Keys [i * page_size, (i + 1) * page_size) of sequence b live in
+ * page block_table[b * pages_per_seq + i] of the page pools:
+ *   kpages, vpages : (num_pages, page_size, Hkv, d) bfloat16
+ *   block_table    : (B, pages_per_seq) int32 on the device; only the
+ *                    entries covering [0, cache_seqlens[b]) are read, and an
+ *                    entry outside [0, num_pages) is clamped into it (no
+ *                    out-of-range read; the result is then unspecified)
+ * Everything else (q, o, lse, cache_seqlens, num_splits, workspace,
+ * results) is as fa_fwd_kvcache with capacity = page_size * pages_per_seq;
+ * on the same keys the two return bitwise-identical results.
+ * page_size must be a positive multiple of 64 (FA_ERR_INVALID_ARG). */
+fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* vpages,
+                                 const int32_t* block_table, const int32_t* cache_seqlens, void* o, float* lse,
+                                 int num_splits, int B, int Hq, int Hkv, int page_size, int pages_per_seq,
+                                 int num_pages, int d, float scale, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Bytes of device workspace fa_bwd needs: two float32 values (D_i and
  * -LSE_i / scale) per (batch, query head, query), the query count rounded
  * up to a multiple of 32. 0 when B, Hq or Nq is not positive. */

@@ -48,6 +48,7 @@ __all__ = [
     "attention",
     "attention_rows",
     "decode",
+    "decode_paged",
     "merge_partials",
     "online_softmax_attention",
     "attention_backward_rows",
@@ -175,6 +176,25 @@ def decode(q, kcache, vcache, seqlens, scale, heads=None):
             O[b, hq] = (P @ _f64(np.asarray(vcache)[b, :n, kv, :]))[0]
             L[b, hq] = lse[0]
     return O, L
+
+
+def decode_paged(q, kpages, vpages, block_table, seqlens, scale, heads=None):
+    """``decode`` over a paged cache.
+
+    pyshine.com FlashAttention code tour (the paged KV cache of the
+    with-kvcache entry point, after PagedAttention): sequence b's cache rows
+    are its pages block_table[b, 0], block_table[b, 1], ... laid end to end.
+    kpages, vpages: (num_pages, page_size, Hkv, d); block_table:
+    (B, pages_per_seq) page indices.
+    """
+    kp = np.asarray(kpages)
+    vp = np.asarray(vpages)
+    bt = np.asarray(block_table)
+    B, pps = bt.shape
+    _, P, Hkv, d = kp.shape
+    kc = kp[bt].reshape(B, pps * P, Hkv, d)
+    vc = vp[bt].reshape(B, pps * P, Hkv, vp.shape[3])
+    return decode(q, kc, vc, seqlens, scale, heads)
 
 
 def merge_partials(o_parts, lse_parts):

@@ -235,6 +235,27 @@ def pin_decode(tol=1e-12):
         assert np.max(np.abs(l[b] - lb[0, :, 0])) <= tol, ("decode LSE", b)
 
 
+def pin_decode_paged(tol=1e-12):
+    """Pages gathered by hand (plain loops) give the brute-force decode."""
+    r = np.random.default_rng(1350)
+    B, P, pps, Hq, Hkv, d = 2, 3, 3, 4, 2, 5
+    num_pages = 8
+    q = r.normal(size=(B, 1, Hq, d))
+    kp = r.normal(size=(num_pages, P, Hkv, d))
+    vp = r.normal(size=(num_pages, P, Hkv, d))
+    bt = np.array([[5, 0, 7], [2, 6, 1]])
+    lens = [7, 4]
+    o, l = O.decode_paged(q, kp, vp, bt, lens, 0.55)
+    for b, n in enumerate(lens):
+        rows_k = [kp[bt[b][i // P]][i % P] for i in range(n)]
+        rows_v = [vp[bt[b][i // P]][i % P] for i in range(n)]
+        kc = np.array(rows_k)[None]
+        vc = np.array(rows_v)[None]
+        ob, lb = brute_attention(q[b:b + 1], kc, vc, False, 0.55)
+        assert np.max(np.abs(o[b] - ob[0, 0])) <= tol, ("paged O", b)
+        assert np.max(np.abs(l[b] - lb[0, :, 0])) <= tol, ("paged LSE", b)
+
+
 def pin_online_recurrence(tol=1e-12):
     """The tiled (m, l, a) recurrence reaches the brute-force result."""
     q, k, v = rng_case(1400, 1, 11, 11, 1, 1, 4, std=3.0)
@@ -327,6 +348,7 @@ ALL_PINS = [
     pin_gqa_repeat,
     pin_split_combine,
     pin_decode,
+    pin_decode_paged,
     pin_online_recurrence,
     pin_backward_torch_autograd,
     pin_backward_finite_differences,

@@ -116,3 +116,36 @@ def test_default_splits():
     assert fa.fa_kvcache_default_splits(4096, 8, 8192, 256, 3) == 1    # capped by the slot budget
     assert fa.fa_kvcache_default_splits(0, 8, 8192, 256, 3) == 1
     assert fa.fa_kvcache_default_splits(2, 1, 1000000, 256, 3) == (1000000 + 1023) // 1024
+
+
+def test_paged_decode_host_validation():
+    L = fa.lib()
+    null = None
+    # page size not a multiple of 64, missing block table: rejected before any HIP call
+    assert L.fa_fwd_kvcache_paged(null, null, null, null, null, null, null, 1, 2, 4, 2, 96, 4, 8, 128, 0.1,
+                                  null, 0, null) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_kvcache_paged(null, null, null, null, null, null, null, 1, 2, 4, 2, 128, 4, 8, 128, 0.1,
+                                  null, 0, null) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_kvcache_paged(null, null, null, null, null, null, null, 1, 2, 4, 2, 0, 4, 8, 128, 0.1,
+                                  null, 0, null) == fa.FA_ERR_INVALID_ARG
+    # B = 0 is a no-op even without buffers
+    assert L.fa_fwd_kvcache_paged(null, null, null, null, null, null, null, 1, 0, 4, 2, 128, 4, 8, 128, 0.1,
+                                  null, 0, null) == fa.FA_OK
+
+
+def test_backward_host_validation():
+    L = fa.lib()
+    null = None
+    args = lambda **kw: dict(dict(B=1, Hq=4, Hkv=2, Nq=64, Nk=64, d=128, causal=0, scale=0.1), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return L.fa_bwd(null, null, null, null, null, null, null, null, null, a["B"], a["Hq"], a["Hkv"], a["Nq"],
+                        a["Nk"], a["d"], a["causal"], a["scale"], null, 0, null)
+    assert call(Hq=3) == fa.FA_ERR_INVALID_ARG       # Hq % Hkv
+    assert call(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert call(scale=0.0) == fa.FA_ERR_INVALID_ARG
+    assert call(causal=2) == fa.FA_ERR_INVALID_ARG
+    assert call() == fa.FA_ERR_INVALID_ARG           # null tensors
+    assert call(B=0) == fa.FA_OK
+    assert fa.fa_bwd_workspace_size(2, 3, 33) == 2 * 2 * 3 * 64 * 4
+    assert fa.fa_bwd_workspace_size(2, 3, 0) == 0

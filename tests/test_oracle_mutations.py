@@ -13,7 +13,7 @@ from oracle import sdpa as O
 
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
                                     "attention_rows", "decode", "merge_partials",
-                                    "online_softmax_attention", "attention_backward_rows")}
+                                    "online_softmax_attention", "attention_backward_rows", "decode_paged")}
 
 
 def _interleaved_groups(hq, Hq, Hkv):
@@ -141,6 +141,11 @@ def _bwd_variant(kind):
     return f
 
 
+def _paged_identity_table(q, kpages, vpages, block_table, seqlens, scale, heads=None):
+    bt = np.asarray(block_table)
+    return _orig["decode_paged"](q, kpages, vpages, np.sort(bt, axis=1), seqlens, scale, heads)
+
+
 MUTATIONS = [
     ("kv_head_of", _interleaved_groups),
     ("visible_mask", _strict_causal),
@@ -160,6 +165,7 @@ MUTATIONS = [
     ("attention_backward_rows", _bwd_variant("unscaled_dk")),
     ("attention_backward_rows", _bwd_variant("dq_from_values")),
     ("attention_backward_rows", _bwd_variant("dv_untransposed")),
+    ("decode_paged", _paged_identity_table),
 ]
 
 
