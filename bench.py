@@ -113,6 +113,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--bwd-steps", type=int, default=50,
                     help="timed fa_bwd calls on the prefill workload after the step loop (0 = skip)")
+    ap.add_argument("--paged-steps", type=int, default=50,
+                    help="timed paged-cache decode calls after the step loop (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (outside the timed "
                          "region) as the known-size reference for HBM byte counters")
@@ -221,6 +223,38 @@ def main():
                "frac": round(b_tf / PEAK_BF16_TFLOPS, 4), "algorithmic_flops_per_launch": 2.5 * prefill_flops(wp),
                "kernels": "bwd_prep_kernel + bwd_dq_kernel + bwd_dkdv_kernel", "steps": args.bwd_steps}
 
+    # The decode workload again over a paged cache (256-row pages in a
+    # shuffled pool, the same keys), timed after the step loop.
+    paged = None
+    if args.paged_steps > 0:
+        P = 256
+        pps = wd["capacity"] // P
+        g = torch.Generator(device="cpu")
+        g.manual_seed(wd["seed"] + 2000)
+        perm = torch.randperm(wd["B"] * pps, generator=g).to(dev)
+        bt = perm.reshape(wd["B"], pps).to(torch.int32).contiguous()
+        inv = torch.argsort(perm)
+        kp = kc.reshape(wd["B"] * pps, P, wd["Hkv"], wd["d"])[inv].contiguous()
+        vp = vc.reshape(wd["B"] * pps, P, wd["Hkv"], wd["d"])[inv].contiguous()
+
+        def pstep():
+            fa.fa_fwd_kvcache_paged(qd, kp, vp, bt, lens, o=od, lse=lsed, num_splits=S, scale=scale_d, workspace=ws)
+        for _ in range(max(3, args.paged_steps // 5)):
+            pstep()
+        torch.cuda.synchronize()
+        pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.paged_steps)]
+        for e0, e1 in pev:
+            e0.record()
+            pstep()
+            e1.record()
+        torch.cuda.synchronize()
+        p_ms = sum(e0.elapsed_time(e1) for e0, e1 in pev) / len(pev)
+        paged = {"value": round(dec_bytes / (p_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "page_size": P,
+                 "mean_launch_ms": round(p_ms, 5), "frac": round(dec_bytes / (p_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                 "steps": args.paged_steps}
+        del kp, vp
+
     traffic = stored_traffic("prefill:" + args.prefill, PREFILL_KERNEL_SOURCE)
     dec_traffic = stored_traffic("decode:" + args.decode, DECODE_KERNEL_SOURCE)
 
@@ -261,6 +295,7 @@ def main():
                          "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": dec_traffic,
                          "algorithmic_bytes_per_launch": dec_bytes, "mean_launch_ms": round(dc_mean, 5)},
             "num_splits": S,
+            "paged": paged,
         },
         "backward": bwd,
         "device": {"name": props.name, "cus": props.multi_processor_count,
