@@ -53,6 +53,9 @@ __all__ = [
     "online_softmax_attention",
     "attention_backward_rows",
     "attention_backward",
+    "window_mask",
+    "attention_window",
+    "attention_varlen",
 ]
 
 
@@ -326,3 +329,68 @@ def attention_backward(q, k, v, do, causal, scale):
             dk[b, :, kv, :] += gk
             dv[b, :, kv, :] += gv
     return dq, dk, dv
+
+
+def window_mask(Nq, Nk, window_left, window_right, rows=None):
+    """Boolean (len(rows), Nk) mask of a bottom-right aligned local window.
+
+    pyshine.com FlashAttention code tour: causal masking is aligned to the
+    bottom right since version 2.1 (the last query sees the last key) and
+    sliding windows arrived in 2.3. With off = Nk - Nq, key j is visible to
+    query i iff i + off - window_left <= j <= i + off + window_right; a
+    negative bound means no limit on that side. Causal (bottom-right) is
+    window_left < 0, window_right = 0.
+    """
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    c = (i + (Nk - Nq))[:, None]
+    m = np.ones((i.shape[0], Nk), dtype=bool)
+    if window_left >= 0:
+        m &= j[None, :] >= c - window_left
+    if window_right >= 0:
+        m &= j[None, :] <= c + window_right
+    return m
+
+
+def attention_window(q, k, v, window_left, window_right, scale):
+    """Attention under ``window_mask``: O (B, Nq, Hq, dv), LSE (B, Hq, Nq).
+
+    Rows that see no key get O = 0 and LSE = -inf (as ``softmax_rows``).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    B, Nq, Hq, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    O = np.zeros((B, Nq, Hq, v.shape[3]))
+    L = np.zeros((B, Hq, Nq))
+    mask = window_mask(Nq, Nk, window_left, window_right)
+    for b in range(B):
+        for hq in range(Hq):
+            kv = kv_head_of(hq, Hq, Hkv)
+            P, lse = softmax_rows(scores(q[b, :, hq], k[b, :, kv], scale), mask)
+            O[b, :, hq] = P @ _f64(v[b, :, kv])
+            L[b, hq] = lse
+    return O, L
+
+
+def attention_varlen(q, k, v, cu_q, cu_k, window_left, window_right, scale):
+    """Packed variable-length batch: sequence b is rows cu_q[b]:cu_q[b+1] of
+    q (total_q, Hq, d) against rows cu_k[b]:cu_k[b+1] of k and v
+    (total_k, Hkv, d) (pyshine.com code tour: variable-length batches
+    since 2.0, the padded batch flattened into packed token arrays).
+    Returns O (total_q, Hq, dv) and LSE (Hq, total_q).
+    """
+    q = np.asarray(q)
+    k = np.asarray(k)
+    v = np.asarray(v)
+    O = np.zeros(q.shape[:2] + (v.shape[2],))
+    L = np.zeros((q.shape[1], q.shape[0]))
+    for b in range(len(cu_q) - 1):
+        qa, qb, ka, kb = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qb == qa:
+            continue
+        o, lse = attention_window(q[None, qa:qb], k[None, ka:kb], v[None, ka:kb], window_left, window_right, scale)
+        O[qa:qb] = o[0]
+        L[:, qa:qb] = lse[0]
+    return O, L

@@ -333,6 +333,99 @@ def pin_backward_gqa_sum(tol=1e-13):
         assert np.max(np.abs(dv - dv2.reshape(1, 5, 2, 3, 3).sum(axis=3))) <= tol, "GQA dv"
 
 
+# ---------------------------------------------------------------------------
+# local windows, bottom-right alignment, variable-length packing
+# ---------------------------------------------------------------------------
+def brute_window(q, k, v, wl, wr, scale):
+    """Plain loops: key j visible to query i iff i+off-wl <= j <= i+off+wr."""
+    q = np.asarray(q, dtype=np.float64).tolist()
+    k = np.asarray(k, dtype=np.float64).tolist()
+    v = np.asarray(v, dtype=np.float64).tolist()
+    B, Nq, Hq, d = len(q), len(q[0]), len(q[0][0]), len(q[0][0][0])
+    Nk, Hkv, dv = len(k[0]), len(k[0][0]), len(v[0][0][0])
+    off = Nk - Nq
+    out = np.zeros((B, Nq, Hq, dv))
+    lse = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        for h in range(Hq):
+            g = (h * Hkv) // Hq
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if (wl < 0 or j >= i + off - wl) and (wr < 0 or j <= i + off + wr)]
+                if not keys:
+                    lse[b, h, i] = -math.inf
+                    continue
+                s = [scale * math.fsum(q[b][i][h][t] * k[b][j][g][t] for t in range(d)) for j in keys]
+                mx = max(s)
+                e = [math.exp(x - mx) for x in s]
+                den = math.fsum(e)
+                lse[b, h, i] = mx + math.log(den)
+                for t in range(dv):
+                    out[b, i, h, t] = math.fsum(e[n] * v[b][j][g][t] for n, j in enumerate(keys)) / den
+    return out, lse
+
+
+def pin_window_brute_force(tol=1e-12):
+    for (Nq, Nk, wl, wr) in ((5, 9, 2, 0), (9, 5, -1, 0), (7, 7, 1, 2), (6, 6, -1, -1), (4, 8, 0, -1), (8, 3, 3, 1)):
+        q, k, v = rng_case(1900 + Nq * 10 + Nk, 1, Nq, Nk, 4, 2, 3, std=1.5)
+        o, l = O.attention_window(q, k, v, wl, wr, 0.6)
+        ob, lb = brute_window(q, k, v, wl, wr, 0.6)
+        fin = np.isfinite(lb)
+        assert np.max(np.abs(o - ob)) <= tol, ("window O", Nq, Nk, wl, wr)
+        assert np.array_equal(fin, np.isfinite(l)) and np.max(np.abs(l[fin] - lb[fin]), initial=0.0) <= tol
+
+
+def pin_window_torch_mask(tol=1e-12):
+    """PyTorch float64 SDPA with the window as an explicit boolean mask."""
+    import torch
+
+    q, k, v = rng_case(2000, 2, 6, 10, 4, 4, 5)
+    for wl, wr in ((3, 0), (-1, 0), (2, 2)):
+        o, _ = O.attention_window(q, k, v, wl, wr, 0.45)
+        i = torch.arange(6)[:, None] + 4
+        j = torch.arange(10)[None, :]
+        m = torch.ones(6, 10, dtype=torch.bool)
+        if wl >= 0:
+            m &= j >= i - wl
+        if wr >= 0:
+            m &= j <= i + wr
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            *(torch.tensor(x).permute(0, 2, 1, 3) for x in (q, k, v)), attn_mask=m, scale=0.45)
+        assert np.max(np.abs(o - ref.permute(0, 2, 1, 3).numpy())) <= tol, ("torch mask", wl, wr)
+
+
+def pin_window_special_cases(tol=0.0):
+    """No window = non-causal; (-1, 0) on square inputs = top-left causal."""
+    q, k, v = rng_case(2100, 1, 7, 7, 2, 1, 4)
+    o1, l1 = O.attention_window(q, k, v, -1, -1, 0.8)
+    o2, l2 = O.attention(q, k, v, False, 0.8)
+    assert np.max(np.abs(o1 - o2)) <= tol and np.max(np.abs(l1 - l2)) <= tol, "no window"
+    o1, l1 = O.attention_window(q, k, v, -1, 0, 0.8)
+    o2, l2 = O.attention(q, k, v, True, 0.8)
+    assert np.max(np.abs(o1 - o2)) <= tol and np.max(np.abs(l1 - l2)) <= tol, "square causal"
+
+
+def pin_varlen_concatenation(tol=0.0):
+    """A packed batch is its sequences' results laid end to end."""
+    r = np.random.default_rng(2200)
+    lq, lk = [3, 0, 5, 2], [4, 2, 5, 6]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = r.normal(size=(cu_q[-1], 4, 3))
+    k = r.normal(size=(cu_k[-1], 2, 3))
+    v = r.normal(size=(cu_k[-1], 2, 3))
+    for wl, wr in ((-1, -1), (-1, 0), (1, 1)):
+        o, l = O.attention_varlen(q, k, v, cu_q, cu_k, wl, wr, 0.7)
+        for b in range(4):
+            if lq[b] == 0:
+                continue
+            ob, lb = brute_window(q[None, cu_q[b]:cu_q[b + 1]], k[None, cu_k[b]:cu_k[b + 1]],
+                                  v[None, cu_k[b]:cu_k[b + 1]], wl, wr, 0.7)
+            assert np.max(np.abs(o[cu_q[b]:cu_q[b + 1]] - ob[0])) <= 1e-12, ("varlen O", b, wl, wr)
+            fin = np.isfinite(lb[0])
+            lv = l[:, cu_q[b]:cu_q[b + 1]]
+            assert np.array_equal(np.isfinite(lv), fin)
+            assert np.max(np.abs(lv[fin] - lb[0][fin]), initial=0.0) <= 1e-12, ("varlen LSE", b)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -354,4 +447,8 @@ ALL_PINS = [
     pin_backward_finite_differences,
     pin_backward_constant_values,
     pin_backward_gqa_sum,
+    pin_window_brute_force,
+    pin_window_torch_mask,
+    pin_window_special_cases,
+    pin_varlen_concatenation,
 ]

@@ -13,7 +13,8 @@ from oracle import sdpa as O
 
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
                                     "attention_rows", "decode", "merge_partials",
-                                    "online_softmax_attention", "attention_backward_rows", "decode_paged")}
+                                    "online_softmax_attention", "attention_backward_rows", "decode_paged",
+                                    "window_mask", "attention_varlen")}
 
 
 def _interleaved_groups(hq, Hq, Hkv):
@@ -146,6 +147,31 @@ def _paged_identity_table(q, kpages, vpages, block_table, seqlens, scale, heads=
     return _orig["decode_paged"](q, kpages, vpages, np.sort(bt, axis=1), seqlens, scale, heads)
 
 
+def _window_top_left(Nq, Nk, window_left, window_right, rows=None):
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    m = np.ones((i.shape[0], Nk), dtype=bool)
+    if window_left >= 0:
+        m &= j[None, :] >= i[:, None] - window_left
+    if window_right >= 0:
+        m &= j[None, :] <= i[:, None] + window_right
+    return m
+
+
+def _window_exclusive(Nq, Nk, window_left, window_right, rows=None):
+    m = _orig["window_mask"](Nq, Nk, window_left, window_right, rows)
+    i = np.arange(Nq) if rows is None else np.asarray(rows)
+    j = np.arange(Nk)
+    if window_left >= 0:
+        m &= j[None, :] > (i + Nk - Nq)[:, None] - window_left
+    return m
+
+
+def _varlen_shared_keys(q, k, v, cu_q, cu_k, window_left, window_right, scale):
+    return _orig["attention_varlen"](q, k, v, cu_q, cu_q if len(cu_q) == len(cu_k) and cu_q[-1] <= cu_k[-1]
+                                     else cu_k, window_left, window_right, scale)
+
+
 MUTATIONS = [
     ("kv_head_of", _interleaved_groups),
     ("visible_mask", _strict_causal),
@@ -166,6 +192,9 @@ MUTATIONS = [
     ("attention_backward_rows", _bwd_variant("dq_from_values")),
     ("attention_backward_rows", _bwd_variant("dv_untransposed")),
     ("decode_paged", _paged_identity_table),
+    ("window_mask", _window_top_left),
+    ("window_mask", _window_exclusive),
+    ("attention_varlen", _varlen_shared_keys),
 ]
 
 
