@@ -17,6 +17,8 @@ __all__ = [
     "fa_abi_version",
     "fa_status_string",
     "fa_fwd",
+    "fa_fwd_window",
+    "fa_fwd_varlen",
     "fa_fwd_kvcache",
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
@@ -57,6 +59,10 @@ def lib():
     L.fa_status_string.argtypes = [i]
     L.fa_fwd.restype = i
     L.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, i, vp]
+    L.fa_fwd_window.restype = i
+    L.fa_fwd_window.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp]
+    L.fa_fwd_varlen.restype = i
+    L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_fwd_kvcache_workspace_size.restype = sz
@@ -143,6 +149,76 @@ def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None, wan
                       int(bool(causal)), float(scale), dt, _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd")
+    return o, lse
+
+
+def fa_fwd_window(q, k, v, window_left=-1, window_right=-1, o=None, lse=None, scale=None, stream=None,
+                  want_lse=True):
+    """Bottom-right aligned local-window attention through ``fa_fwd_window``.
+
+    q: (B, Nq, Hq, d); k, v: (B, Nk, Hkv, d); bf16. Key j is visible to
+    query i iff i + (Nk - Nq) - window_left <= j <= i + (Nk - Nq) +
+    window_right (negative: unlimited). Returns (o, lse (B, Hq, Nq)).
+    """
+    import torch
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be (batch, seq, heads, head_dim)")
+    B, Nq, Hq, d = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Nk, Hkv, d) or tuple(v.shape) != (B, Nk, Hkv, d):
+        raise ValueError("k/v shapes do not match q")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, q.device)
+    o = torch.empty_like(q) if o is None else o
+    _check(o, "o", torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
+                             int(window_left), int(window_right), float(scale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_window")
+    return o, lse
+
+
+def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, window_left=-1, window_right=-1, o=None,
+                  lse=None, scale=None, stream=None, want_lse=True):
+    """Packed variable-length batch through ``fa_fwd_varlen``.
+
+    q: (total_q, Hq, d); k, v: (total_k, Hkv, d); bf16; cu_seqlens_*:
+    (B + 1,) int32 on the same GPU. Returns (o (total_q, Hq, d),
+    lse (Hq, total_q)).
+    """
+    import torch
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be (tokens, heads, head_dim)")
+    total_q, Hq, d = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    if tuple(v.shape) != tuple(k.shape) or k.shape[2] != d:
+        raise ValueError("k/v shapes do not match q")
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _check(t, n, torch.bfloat16, q.device)
+    for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        _check(t, n, torch.int32, q.device)
+    B = cu_seqlens_q.numel() - 1
+    if B < 0 or cu_seqlens_k.numel() != B + 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be (B + 1,)")
+    o = torch.empty_like(q) if o is None else o
+    _check(o, "o", torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                             B, Hq, Hkv, int(max_seqlen_q), total_q, total_k, d, int(window_left),
+                             int(window_right), float(scale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_varlen")
     return o, lse
 
 

@@ -68,8 +68,80 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   a.d = d;
   a.causal = causal;
   a.scale = scale;
+  a.window_left = -1;
+  a.window_right = causal ? 0 : -1;
+  a.bottom_right = 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return launch_status(dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(a, s) : fa::launch_fwd_f32(a, s));
+}
+
+fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                          int window_left, int window_right, float scale, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!fa::fwd_bf16_supported(d)) return FA_ERR_UNSUPPORTED;
+  if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = 0;
+  a.scale = scale;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_right = window_right < 0 ? -1 : window_right;
+  a.bottom_right = 1;
+  return launch_status(fa::launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int max_seqlen_q, int total_q, int total_k, int d,
+                          int window_left, int window_right, float scale, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || max_seqlen_q < 0 || total_q < 0 || total_k < 0 || d <= 0)
+    return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!fa::fwd_bf16_supported(d)) return FA_ERR_UNSUPPORTED;
+  if ((((int64_t)max_seqlen_q + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535)
+    return FA_ERR_UNSUPPORTED;
+  if (B == 0 || max_seqlen_q == 0 || total_q == 0) return FA_OK;
+  if (q == nullptr || o == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERR_INVALID_ARG;
+  if (total_k > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
+  fa::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = max_seqlen_q;
+  a.Nk = 0;
+  a.d = d;
+  a.causal = 0;
+  a.scale = scale;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_right = window_right < 0 ? -1 : window_right;
+  a.bottom_right = 1;
+  a.cu_q = cu_seqlens_q;
+  a.cu_k = cu_seqlens_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
+  return launch_status(fa::launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits) {

@@ -47,8 +47,17 @@ struct FwdParams {
   const char* __restrict__ v;
   char* __restrict__ o;
   float* __restrict__ lse;
-  int Nq, Nk, Hq, Hkv, group, B;
-  int causal;
+  int Nq, Nk, Hq, Hkv, group, B;  // dense lengths (packed batches: Nq = longest sequence)
+  // visible keys of query i: i + off - wl <= j <= i + off + wr (a negative
+  // bound is unlimited), off = Nk_b - Nq_b when bottom_right, else 0;
+  // top-left causal is (wl, wr) = (-1, 0)
+  int wl, wr, bottom_right;
+  int lpt;           // longest-first order (later query tiles see more keys)
+  // packed variable-length batch: sequence b is rows cu_q[b] .. cu_q[b+1]
+  // of q / o and cu_k[b] .. cu_k[b+1] of k / v; null for the dense layout
+  const int32_t* __restrict__ cu_q;
+  const int32_t* __restrict__ cu_k;
+  int total_q, total_k;  // packed row counts (LSE is then (Hq, total_q))
   int n_qtiles;
   float c;  // scale * log2(e)
 };
@@ -106,20 +115,38 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   const int b = pr / p.Hkv;
   const int kvh = pr - b * p.Hkv;
   const int hq = kvh * p.group + j;
-  const int qt = p.causal ? p.n_qtiles - 1 - r : r;
+  const int qt = p.lpt ? p.n_qtiles - 1 - r : r;
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32 * QB;  // first query row of this wavefront
 
   const int64_t q_row = (int64_t)p.Hq * D * 2;    // bytes between query rows
   const int kv_row = p.Hkv * D * 2;                // bytes between key rows
 
-  int kend = p.Nk;
-  if (p.causal) kend = min(kend, q0 + C::BM);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // this sequence's rows (packed batches clamp the offsets into range)
+  int qrow0, Nqb, krow0, Nkb;
+  if (p.cu_q != nullptr) {
+    qrow0 = min(max(p.cu_q[b], 0), p.total_q);
+    Nqb = min(min(max(p.cu_q[b + 1], qrow0), p.total_q) - qrow0, p.Nq);
+    krow0 = min(max(p.cu_k[b], 0), p.total_k);
+    Nkb = min(max(p.cu_k[b + 1], krow0), p.total_k) - krow0;
+  } else {
+    qrow0 = b * p.Nq;
+    Nqb = p.Nq;
+    krow0 = b * p.Nk;
+    Nkb = p.Nk;
+  }
+  if (q0 >= Nqb) return;  // whole workgroup: past this sequence's queries
+  const int off = p.bottom_right ? Nkb - Nqb : 0;
+  // keys some row of the tile sees: tiles t0 .. t0 + ntiles - 1
+  const int q_last = min(q0 + C::BM, Nqb) - 1;
+  const int klo = p.wl >= 0 ? max(q0 + off - p.wl, 0) : 0;
+  const int khi = p.wr >= 0 ? min(q_last + off + p.wr, Nkb - 1) : Nkb - 1;
+  const int t0 = klo / BN;
+  const int ntiles = khi >= klo ? khi / BN - t0 + 1 : 0;
 
   // ---- DMA addressing: load j of a tile fills slot j*THREADS + tid
-  const char* kbase = p.k + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
-  const char* vbase = p.v + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  const char* kbase = p.k + ((int64_t)krow0 * p.Hkv + kvh) * D * 2;
+  const char* vbase = p.v + ((int64_t)krow0 * p.Hkv + kvh) * D * 2;
   // load j of a tile fills slot s = j*THREADS + tid, i.e. row s / CPR; the
   // byte offsets of full tiles are computed once
   int dma_row[C::DMA], dma_col[C::DMA];
@@ -134,17 +161,17 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
 
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    const int j0 = t * BN;
+    const int j0 = (t0 + t) * BN;
     const char* ks = kbase + (int64_t)j0 * kv_row;
     const char* vs = vbase + (int64_t)j0 * kv_row;
     const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::TILE_BYTES);
-    if (j0 + BN <= p.Nk) {  // uniform: full tile
+    if (j0 + BN <= Nkb) {  // uniform: full tile
 #pragma unroll
       for (int j = 0; j < C::DMA; ++j) dma16(ks, dma_off[j], st + j * C::THREADS * 16);
 #pragma unroll
       for (int j = 0; j < C::DMA; ++j) dma16(vs, dma_off[j], st + C::V_REGION + j * C::THREADS * 16);
     } else {
-      const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
+      const int last = Nkb - 1 - j0;  // rows past the end re-read the last key (masked later)
 #pragma unroll
       for (int j = 0; j < C::DMA; ++j)
         dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * C::THREADS * 16);
@@ -164,10 +191,10 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const int row = qw0 + qb * 32 + r32;
-    const char* qrow = p.q + ((int64_t)b * p.Nq + row) * q_row + (int64_t)hq * D * 2;
+    const char* qrow = p.q + ((int64_t)qrow0 + row) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      qf[qb][ks] = row < p.Nq ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
+      qf[qb][ks] = row < Nqb ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
   wait_vm_loads();
@@ -260,21 +287,23 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   // accumulator, probabilities and their row sums, P^T packed to bf16
   auto softmax_phase = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const int j0 = t * BN;
+    const int j0 = (t0 + t) * BN;
     bool moved = false;
     float alpha[QB], m_cand[QB];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if constexpr (MASK) {
-        // key j0 + 4g + off (off = 32 nb + 8 (i/4) + i%4) is visible iff off <= lim
+        // key j0 + 4g + o (o = 32 nb + 8 (i/4) + i%4) is visible iff lo <= o <= hi
         const int my_q = qw0 + qb * 32 + r32;
-        const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - j0 - 4 * g;
+        const int base = j0 + 4 * g;
+        const int lo = (p.wl >= 0 ? my_q + off - p.wl : 0) - base;
+        const int hi = (p.wr >= 0 ? min(my_q + off + p.wr, Nkb - 1) : Nkb - 1) - base;
 #pragma unroll
         for (int nb = 0; nb < NBT; ++nb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int off = nb * 32 + 8 * (i >> 2) + (i & 3);
-            if (off > lim) sc[qb][nb][i] = -INFINITY;
+            const int o = nb * 32 + 8 * (i >> 2) + (i & 3);
+            if (o < lo || o > hi) sc[qb][nb][i] = -INFINITY;
           }
       }
       float mx = -INFINITY;
@@ -382,28 +411,46 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     }
   };
 
-  int nt_w = ntiles;
-  int nt_full = p.Nk / BN;
-  if (p.causal) {
-    nt_w = min(ntiles, (qw0 + 32 * QB - 1) / BN + 1);  // tiles holding a key <= this wave's last row
-    nt_full = min(nt_full, (qw0 + 1) / BN);            // tiles entirely <= this wave's first row
+  // This wavefront's tiles (relative to t0): [t_lo, t_hi) hold a key some
+  // of its rows see, [u_lo, u_hi) only keys all of its rows see (no mask).
+  int t_lo = 0, t_hi = 0, u_lo = 0, u_hi = 0;
+  {
+    const int wq_last = min(qw0 + 32 * QB, Nqb) - 1;
+    const int wlo = p.wl >= 0 ? max(qw0 + off - p.wl, 0) : 0;
+    const int whi = p.wr >= 0 ? min(wq_last + off + p.wr, Nkb - 1) : Nkb - 1;
+    if (wq_last >= qw0 && whi >= wlo) {
+      t_lo = max(wlo / BN - t0, 0);
+      t_hi = min(whi / BN - t0 + 1, ntiles);
+      const int flo = p.wl >= 0 ? max(wq_last + off - p.wl, 0) : 0;
+      const int fhi = p.wr >= 0 ? min(qw0 + off + p.wr, Nkb - 1) : Nkb - 1;
+      u_lo = min(max((flo + BN - 1) / BN - t0, t_lo), t_hi);
+      u_hi = min(max((fhi + 1) / BN - t0, u_lo), t_hi);
+    }
   }
-  nt_full = min(nt_full, nt_w);
   int t = 0;
-  // unmasked tiles NST at a time: tile t + S sits in stage S
+  for (; t < t_lo; ++t) sync_tile(t);
+  for (; t < u_lo; ++t) {
+    sync_tile(t);
+    compute_any(t, std::true_type{});
+  }
   if constexpr (C::CONST_STAGE) {
-    for (; t + NST <= nt_full; t += NST) {
+    for (; t < u_hi && t % NST != 0; ++t) {
+      sync_tile(t);
+      compute_any(t, std::false_type{});
+    }
+    // unmasked tiles NST at a time: tile t + S sits in stage S
+    for (; t + NST <= u_hi; t += NST) {
       static_for<NST>([&](auto S) {
         sync_tile(t + decltype(S)::value);
         compute_tile(t + decltype(S)::value, std::false_type{}, S);
       });
     }
   }
-  for (; t < nt_full; ++t) {
+  for (; t < u_hi; ++t) {
     sync_tile(t);
     compute_any(t, std::false_type{});
   }
-  for (; t < nt_w; ++t) {
+  for (; t < t_hi; ++t) {
     sync_tile(t);
     compute_any(t, std::true_type{});
   }
@@ -415,8 +462,8 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     const int my_q = qw0 + qb * 32 + r32;
     const float lt = halves_sum(l[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (my_q < p.Nq) {
-      char* orow = p.o + ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
+    if (my_q < Nqb) {
+      char* orow = p.o + ((int64_t)qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
@@ -429,7 +476,8 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
         }
       }
       if (p.lse != nullptr && g == 0) {
-        p.lse[((int64_t)b * p.Hq + hq) * p.Nq + my_q] =
+        const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
+        p.lse[lrow + my_q] =
             lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
       }
     }
@@ -449,7 +497,14 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.group = a.Hq / a.Hkv;
-  p.causal = a.causal;
+  p.wl = a.window_left;
+  p.wr = a.window_right;
+  p.bottom_right = a.bottom_right;
+  p.lpt = a.window_right >= 0;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.n_qtiles = (a.Nq + C::BM - 1) / C::BM;
   p.c = a.scale * kLog2e;
   p.B = a.B;

@@ -18,8 +18,17 @@ struct FwdArgs {
   void* o;
   float* lse;  // may be null
   int B, Hq, Hkv, Nq, Nk, d;
-  int causal;
+  int causal;  // top-left causal; the bf16 kernel reads the window fields below
   float scale;
+  // key j is visible to query i iff i + off - window_left <= j <=
+  // i + off + window_right (negative: unlimited), off = Nk_b - Nq_b when
+  // bottom_right, else 0
+  int window_left = -1, window_right = -1, bottom_right = 0;
+  // packed variable-length batch (null: dense); Nq is then the longest
+  // query sequence
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 struct DecodeArgs {

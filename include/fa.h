@@ -132,6 +132,38 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
  * per resident slot. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);
 
+/* fa_fwd with a local window, aligned to the bottom-right corner
+ * (pyshine.com FlashAttention code tour: bottom-right causal alignment
+ * since 2.1, sliding windows since 2.3). Key j is visible to query i iff
+ *     i + off - window_left <= j <= i + off + window_right,  off = Nk - Nq;
+ * a negative bound is unlimited. (-1, 0) is bottom-right causal (for
+ * Nq == Nk the same as fa_fwd's causal), (-1, -1) no mask, (w, 0) a
+ * causal sliding window of w + 1 keys. Rows that see no key get O = 0 and
+ * LSE = -inf. bfloat16 only, d in {64, 128, 256}; other arguments and
+ * errors as fa_fwd. */
+fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d,
+                          int window_left, int window_right, float scale, void* stream);
+
+/* fa_fwd_window over a packed variable-length batch (pyshine.com code
+ * tour: variable-length batches since 2.0; padded batches are flattened
+ * into packed token arrays). Sequence b is rows cu_seqlens_q[b] ..
+ * cu_seqlens_q[b+1]-1 of q and o, (total_q, Hq, d) bfloat16, against rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v, (total_k, Hkv, d);
+ * the window is aligned to each sequence's own bottom-right corner.
+ *   cu_seqlens_q, cu_seqlens_k : (B + 1,) int32 on the device, nondecreasing,
+ *                                starting at 0 and ending at total_q / total_k
+ *   max_seqlen_q               : the longest query sequence (the grid covers
+ *                                that many rows per sequence; longer ones are
+ *                                cut there)
+ *   lse                        : (Hq, total_q) float32, or NULL
+ * Offsets outside [0, total] are clamped, so no access leaves the arrays.
+ * bfloat16 only, d in {64, 128, 256}. */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int max_seqlen_q, int total_q, int total_k, int d,
+                          int window_left, int window_right, float scale, void* stream);
+
 /* fa_fwd_kvcache over a paged cache (pyshine.com FlashAttention code tour:
  * the paged KV cache of flash_attn_with_kvcache, after the PagedAttention
  * layout). Keys [i * page_size, (i + 1) * page_size) of sequence b live in
