@@ -56,6 +56,7 @@ __all__ = [
     "window_mask",
     "attention_window",
     "attention_varlen",
+    "decode_append",
 ]
 
 
@@ -394,3 +395,51 @@ def attention_varlen(q, k, v, cu_q, cu_k, window_left, window_right, scale):
         O[qa:qb] = o[0]
         L[:, qa:qb] = lse[0]
     return O, L
+
+
+def decode_append(q, kcache, vcache, seqlens, k_new, v_new, causal, scale):
+    """A decode step that first writes the new tokens' keys and values into
+    the cache, then attends to the grown cache.
+
+    pyshine.com FlashAttention code tour, "Why You Need This" and its usage
+    example: the with-kvcache entry point takes a preallocated cache with
+    per-sequence lengths and updates it in place with the new tokens; causal
+    masking is bottom-right aligned (version 2.1). FlashAttention: Part 2,
+    section 4.1: the step then reads the whole cache.
+
+    q: (B, Nq, Hq, d); kcache, vcache: (B, capacity, Hkv, d); seqlens: (B,)
+    rows already in the cache; k_new, v_new: (B, Nq, Hkv, d) or both None
+    (nothing appended). Readings where the pages are silent: a length is
+    clamped to [0, capacity]; new rows at or past capacity are dropped;
+    with n = length + appended rows, query i sees key j iff j < min(n,
+    capacity) and, when causal, j <= n - Nq + i; a query that sees no key
+    gets O = 0 and LSE = -inf.
+    Returns (kcache', vcache', O (B, Nq, Hq, dv), LSE (B, Hq, Nq)); the
+    inputs are not modified.
+    """
+    q = _f64(q)
+    kc = _f64(kcache).copy()
+    vc = _f64(vcache).copy()
+    B, Nq, Hq, _ = q.shape
+    cap, Hkv = kc.shape[1], kc.shape[2]
+    n_new = 0 if k_new is None else Nq
+    O = np.zeros((B, Nq, Hq, vc.shape[3]))
+    L = np.zeros((B, Hq, Nq))
+    for b in range(B):
+        base = min(max(int(seqlens[b]), 0), cap)
+        for i in range(n_new):
+            if base + i < cap:
+                kc[b, base + i] = _f64(k_new)[b, i]
+                vc[b, base + i] = _f64(v_new)[b, i]
+        n = base + n_new
+        avail = min(n, cap)
+        j = np.arange(avail)
+        mask = np.ones((Nq, avail), dtype=bool)
+        if causal:
+            mask &= j[None, :] <= (n - Nq + np.arange(Nq))[:, None]
+        for hq in range(Hq):
+            kv = kv_head_of(hq, Hq, Hkv)
+            P, lse = softmax_rows(scores(q[b, :, hq], kc[b, :avail, kv], scale), mask)
+            O[b, :, hq] = P @ vc[b, :avail, kv]
+            L[b, hq] = lse
+    return kc, vc, O, L

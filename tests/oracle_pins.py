@@ -426,6 +426,83 @@ def pin_varlen_concatenation(tol=0.0):
             assert np.max(np.abs(lv[fin] - lb[0][fin]), initial=0.0) <= 1e-12, ("varlen LSE", b)
 
 
+# ---------------------------------------------------------------------------
+# decode step with in-place cache append
+# ---------------------------------------------------------------------------
+def _append_case(seed, B, cap, Nq, Hq, Hkv, d):
+    r = np.random.default_rng(seed)
+    return (r.normal(size=(B, Nq, Hq, d)), r.normal(size=(B, cap, Hkv, d)), r.normal(size=(B, cap, Hkv, d)),
+            r.normal(size=(B, Nq, Hkv, d)), r.normal(size=(B, Nq, Hkv, d)))
+
+
+def pin_decode_append_brute_force(tol=1e-12):
+    """Cache rows gathered by hand, then the new rows, attended by the
+    bottom-right brute force (plain loops)."""
+    B, cap, Nq, Hq, Hkv, d = 3, 9, 3, 4, 2, 3
+    q, kc, vc, kn, vn = _append_case(2300, B, cap, Nq, Hq, Hkv, d)
+    lens = [2, 0, 6]
+    for append in (True, False):
+        for causal in (True, False):
+            k2, v2, o, l = O.decode_append(q, kc, vc, lens, kn if append else None, vn if append else None,
+                                           causal, 0.6)
+            for b in range(B):
+                rows_k = [kc[b, j] for j in range(lens[b])] + ([kn[b, i] for i in range(Nq)] if append else [])
+                rows_v = [vc[b, j] for j in range(lens[b])] + ([vn[b, i] for i in range(Nq)] if append else [])
+                if not rows_k:  # nothing to attend: O = 0, LSE = -inf
+                    assert not np.any(o[b]) and np.all(l[b] == -np.inf), ("empty cache", append, causal, b)
+                    continue
+                ob, lb = brute_window(q[b:b + 1], np.array(rows_k)[None], np.array(rows_v)[None], -1,
+                                      0 if causal else -1, 0.6)
+                assert np.max(np.abs(o[b] - ob[0])) <= tol, ("append O", append, causal, b)
+                fin = np.isfinite(lb[0])
+                assert np.array_equal(np.isfinite(l[b]), fin), ("rows without keys", append, causal, b)
+                assert np.max(np.abs(l[b][fin] - lb[0][fin]), initial=0.0) <= tol, ("append LSE", b)
+
+
+def pin_decode_append_cache_update(tol=0.0):
+    """New rows land at [len, len + Nq); every other row, and the inputs,
+    stay as they were; rows at or past capacity are dropped."""
+    B, cap, Nq, Hq, Hkv, d = 3, 6, 3, 2, 1, 2
+    q, kc, vc, kn, vn = _append_case(2310, B, cap, Nq, Hq, Hkv, d)
+    kc0, vc0 = kc.copy(), vc.copy()
+    lens = [1, 4, 6]
+    k2, v2, _, _ = O.decode_append(q, kc, vc, lens, kn, vn, True, 1.0)
+    assert np.array_equal(kc, kc0) and np.array_equal(vc, vc0), "inputs modified"
+    for b in range(B):
+        for j in range(cap):
+            i = j - lens[b]
+            want_k = kn[b, i] if 0 <= i < Nq else kc0[b, j]
+            want_v = vn[b, i] if 0 <= i < Nq else vc0[b, j]
+            assert np.array_equal(k2[b, j], want_k) and np.array_equal(v2[b, j], want_v), ("cache row", b, j)
+
+
+def pin_decode_append_reduces_to_decode(tol=1e-12):
+    """One query: without new rows this is the plain decode; with one new
+    row it is the plain decode of the grown cache at length + 1."""
+    B, cap, Hq, Hkv, d = 2, 8, 4, 2, 3
+    q, kc, vc, kn, vn = _append_case(2320, B, cap, 1, Hq, Hkv, d)
+    lens = [5, 7]
+    _, _, o, l = O.decode_append(q, kc, vc, lens, None, None, True, 0.8)
+    od, ld = O.decode(q, kc, vc, lens, 0.8)
+    assert np.max(np.abs(o[:, 0] - od)) <= tol and np.max(np.abs(l[:, :, 0] - ld)) <= tol
+    k2, v2, o, l = O.decode_append(q, kc, vc, lens, kn, vn, True, 0.8)
+    od, ld = O.decode(q, k2, v2, [n + 1 for n in lens], 0.8)
+    assert np.max(np.abs(o[:, 0] - od)) <= tol and np.max(np.abs(l[:, :, 0] - ld)) <= tol
+
+
+def pin_decode_append_capacity_overflow(tol=1e-12):
+    """Length cap - 1 plus three new rows: only the first is written and all
+    three queries see the full cache (their causal limits lie past it)."""
+    B, cap, Nq, Hq, Hkv, d = 1, 5, 3, 2, 1, 3
+    q, kc, vc, kn, vn = _append_case(2330, B, cap, Nq, Hq, Hkv, d)
+    k2, v2, o, l = O.decode_append(q, kc, vc, [cap - 1], kn, vn, True, 0.9)
+    assert np.array_equal(k2[0, cap - 1], kn[0, 0]) and np.array_equal(v2[0, cap - 1], vn[0, 0])
+    rows_k = np.array([kc[0, j] for j in range(cap - 1)] + [kn[0, 0]])[None]
+    rows_v = np.array([vc[0, j] for j in range(cap - 1)] + [vn[0, 0]])[None]
+    ob, lb = brute_attention(q, rows_k, rows_v, False, 0.9)
+    assert np.max(np.abs(o - ob)) <= tol and np.max(np.abs(l - lb)) <= tol
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -451,4 +528,8 @@ ALL_PINS = [
     pin_window_torch_mask,
     pin_window_special_cases,
     pin_varlen_concatenation,
+    pin_decode_append_brute_force,
+    pin_decode_append_cache_update,
+    pin_decode_append_reduces_to_decode,
+    pin_decode_append_capacity_overflow,
 ]

@@ -14,7 +14,7 @@ from oracle import sdpa as O
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
                                     "attention_rows", "decode", "merge_partials",
                                     "online_softmax_attention", "attention_backward_rows", "decode_paged",
-                                    "window_mask", "attention_varlen")}
+                                    "window_mask", "attention_varlen", "decode_append")}
 
 
 def _interleaved_groups(hq, Hq, Hkv):
@@ -172,6 +172,41 @@ def _varlen_shared_keys(q, k, v, cu_q, cu_k, window_left, window_right, scale):
                                      else cu_k, window_left, window_right, scale)
 
 
+def _append_variant(kind):
+    """decode_append with one planted mistake."""
+    def f(q, kcache, vcache, seqlens, k_new, v_new, causal, scale):
+        q = np.asarray(q, dtype=np.float64)
+        kc = np.array(kcache, dtype=np.float64)
+        vc = np.array(vcache, dtype=np.float64)
+        B, Nq, Hq, _ = q.shape
+        cap, Hkv = kc.shape[1], kc.shape[2]
+        n_new = 0 if k_new is None else Nq
+        O_ = np.zeros((B, Nq, Hq, vc.shape[3]))
+        L_ = np.zeros((B, Hq, Nq))
+        for b in range(B):
+            base = min(max(int(seqlens[b]), 0), cap)
+            at = base + 1 if kind == "shifted_write" else base
+            for i in range(n_new):
+                if at + i < cap:
+                    kc[b, at + i] = k_new[b, i]
+                    vc[b, at + i] = v_new[b, i]
+            n = base + n_new
+            avail = min(n, cap) if kind != "old_length" else base
+            j = np.arange(avail)
+            mask = np.ones((Nq, avail), dtype=bool)
+            if causal:
+                lim = np.arange(Nq) if kind == "top_left" else n - Nq + np.arange(Nq)
+                mask &= j[None, :] <= lim[:, None]
+            for hq in range(Hq):
+                kv = O.kv_head_of(hq, Hq, Hkv)
+                P_, lse = O.softmax_rows(O.scores(q[b, :, hq], kc[b, :avail, kv], scale), mask)
+                O_[b, :, hq] = P_ @ vc[b, :avail, kv]
+                L_[b, hq] = lse
+        return kc, vc, O_, L_
+    f.__name__ = f"_append_{kind}"
+    return f
+
+
 MUTATIONS = [
     ("kv_head_of", _interleaved_groups),
     ("visible_mask", _strict_causal),
@@ -195,6 +230,9 @@ MUTATIONS = [
     ("window_mask", _window_top_left),
     ("window_mask", _window_exclusive),
     ("attention_varlen", _varlen_shared_keys),
+    ("decode_append", _append_variant("shifted_write")),
+    ("decode_append", _append_variant("old_length")),
+    ("decode_append", _append_variant("top_left")),
 ]
 
 
