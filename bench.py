@@ -8,10 +8,13 @@ uniform in [1024, 8192]). Inputs are generated on the device before the
 timed region. Each launch is bracketed by HIP events on the stream it runs
 on; `value` is the prefill's algorithmic TFLOP/s (4*B*H*Nq*Nk*d, halved for
 causal) over its mean event time, and the decode's algorithmic GB/s is
-reported beside it. Prints one JSON line.
+reported beside it. After the step loop, and outside its clock, the
+backward, the paged-cache decode and decode steps that append 1 or 4 new
+tokens per sequence are timed on the same workloads. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill NAME]
-                    [--no-cpu-baseline] [--splits S]
+                    [--no-cpu-baseline] [--splits S] [--bwd-steps N]
+                    [--paged-steps N] [--append-steps N]
 """
 
 import argparse
@@ -113,6 +116,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--bwd-steps", type=int, default=50,
                     help="timed fa_bwd calls on the prefill workload after the step loop (0 = skip)")
+    ap.add_argument("--append-steps", type=int, default=50,
+                    help="timed decode-with-append calls (1 and 4 new tokens per sequence) after the step loop "
+                         "(0 = skip)")
     ap.add_argument("--paged-steps", type=int, default=50,
                     help="timed paged-cache decode calls after the step loop (0 = skip)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -255,6 +261,47 @@ def main():
                  "steps": args.paged_steps}
         del kp, vp
 
+    # Decode steps that append 1 or 4 new tokens per sequence to the same
+    # cache (the write happens inside the split kernel), queries bottom-right
+    # causal; lengths are capped so the new rows fit. Bytes: the visible
+    # cache rows read, the new rows read and written, q, o, lse, lengths.
+    append = None
+    if args.append_steps > 0:
+        append = {}
+        for nq in (1, 4):
+            lens_a = torch.clamp(lens, max=wd["capacity"] - nq).contiguous()
+            g = torch.Generator(device=dev)
+            g.manual_seed(wd["seed"] + 3000 + nq)
+            qa = torch.randn((wd["B"], nq, wd["Hq"], wd["d"]), generator=g, device=dev).to(torch.bfloat16)
+            kn = torch.randn((wd["B"], nq, wd["Hkv"], wd["d"]), generator=g, device=dev).to(torch.bfloat16)
+            vn = torch.randn((wd["B"], nq, wd["Hkv"], wd["d"]), generator=g, device=dev).to(torch.bfloat16)
+            oa = torch.empty_like(qa)
+            la = torch.empty((wd["B"], wd["Hq"], nq), dtype=torch.float32, device=dev)
+            wsa = torch.empty(max(fa.fa_fwd_kvcache_workspace_size(wd["B"] * nq, wd["Hq"], wd["d"], S), 1),
+                              dtype=torch.uint8, device=dev)
+            rows = int(lens_a.to(torch.int64).sum().item()) + wd["B"] * nq
+            a_bytes = (rows * wd["Hkv"] * wd["d"] * 2 * 2 + 2 * kn.numel() * 2 * 2
+                       + qa.numel() * 2 + oa.numel() * 2 + la.numel() * 4 + lens.numel() * 4)
+
+            def astep():
+                fa.fa_fwd_kvcache_append(qa, kc, vc, lens_a, kn, vn, causal=True, o=oa, lse=la, num_splits=S,
+                                         scale=scale_d, workspace=wsa)
+            for _ in range(max(3, args.append_steps // 5)):
+                astep()
+            torch.cuda.synchronize()
+            aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(args.append_steps)]
+            for e0, e1 in aev:
+                e0.record()
+                astep()
+                e1.record()
+            torch.cuda.synchronize()
+            a_ms = sum(e0.elapsed_time(e1) for e0, e1 in aev) / len(aev)
+            a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
+            append[f"q{nq}"] = {"value": round(a_gbs, 1), "unit": "GB/s", "queries_per_seq": nq,
+                                "mean_launch_ms": round(a_ms, 5), "frac": round(a_gbs / PEAK_HBM_GBS, 4),
+                                "algorithmic_bytes_per_launch": a_bytes, "steps": args.append_steps}
+
     traffic = stored_traffic("prefill:" + args.prefill, PREFILL_KERNEL_SOURCE)
     dec_traffic = stored_traffic("decode:" + args.decode, DECODE_KERNEL_SOURCE)
 
@@ -296,6 +343,7 @@ def main():
                          "algorithmic_bytes_per_launch": dec_bytes, "mean_launch_ms": round(dc_mean, 5)},
             "num_splits": S,
             "paged": paged,
+            "append": append,
         },
         "backward": bwd,
         "device": {"name": props.name, "cus": props.multi_processor_count,

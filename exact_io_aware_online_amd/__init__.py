@@ -23,6 +23,8 @@ __all__ = [
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
     "fa_fwd_kvcache_paged",
+    "fa_fwd_kvcache_append",
+    "fa_fwd_kvcache_paged_append",
     "fa_bwd",
     "fa_bwd_workspace_size",
     "FA_DTYPE_BF16",
@@ -71,6 +73,11 @@ def lib():
     L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i]
     L.fa_fwd_kvcache_paged.restype = i
     L.fa_fwd_kvcache_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_fwd_kvcache_append.restype = i
+    L.fa_fwd_kvcache_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_fwd_kvcache_paged_append.restype = i
+    L.fa_fwd_kvcache_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f,
+                                              vp, sz, vp]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd_workspace_size.argtypes = [i, i, i]
     L.fa_bwd.restype = i
@@ -316,6 +323,99 @@ def fa_fwd_kvcache_paged(q, kpages, vpages, block_table, cache_seqlens, o=None, 
                                     num_pages, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache_paged")
+    return o, lse
+
+
+def _append_common(q, k_new, v_new, cache_seqlens, Hkv, d, cap, o, lse, num_splits, workspace, want_lse):
+    import torch
+    if q.dim() != 4:
+        raise ValueError("q must be (batch, queries, heads, head_dim)")
+    B, Nq, Hq, dq = q.shape
+    if dq != d:
+        raise ValueError("cache head_dim does not match q")
+    _check(q, "q", torch.bfloat16, q.device)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+            _check(t, n, torch.bfloat16, q.device)
+            if tuple(t.shape) != (B, Nq, Hkv, d):
+                raise ValueError(f"{n} must be (B, Nq, Hkv, d)")
+    _check(cache_seqlens, "cache_seqlens", torch.int32, q.device)
+    if tuple(cache_seqlens.shape) != (B,):
+        raise ValueError("cache_seqlens must be (B,)")
+    if num_splits is None:
+        num_splits = fa_kvcache_default_splits(B, Hkv, cap)
+    if o is None:
+        o = torch.empty_like(q)
+    _check(o, "o", torch.bfloat16, q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+    need = fa_fwd_kvcache_workspace_size(B * Nq, Hq, d, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return B, Nq, Hq, o, lse, int(num_splits), workspace, ws_bytes
+
+
+def fa_fwd_kvcache_append(q, kcache, vcache, cache_seqlens, k_new=None, v_new=None, causal=True, o=None, lse=None,
+                          num_splits=None, scale=None, workspace=None, stream=None, want_lse=True):
+    """Decode step with in-place cache append through ``fa_fwd_kvcache_append``.
+
+    q: (B, Nq, Hq, d) bf16; kcache, vcache: (B, capacity, Hkv, d) bf16,
+    written in place at rows cache_seqlens[b] .. + Nq - 1 when k_new, v_new
+    (B, Nq, Hkv, d) are given; cache_seqlens: (B,) int32, not advanced.
+    Returns (o (B, Nq, Hq, d) bf16, lse (B, Hq, Nq) float32).
+    """
+    import torch
+    _, cap, Hkv, d = kcache.shape
+    if tuple(vcache.shape) != tuple(kcache.shape) or kcache.shape[0] != q.shape[0]:
+        raise ValueError("cache shapes do not match q")
+    for t, n in ((kcache, "kcache"), (vcache, "vcache")):
+        _check(t, n, torch.bfloat16, q.device)
+    B, Nq, Hq, o, lse, S, workspace, ws_bytes = _append_common(q, k_new, v_new, cache_seqlens, Hkv, d, cap, o, lse,
+                                                                num_splits, workspace, want_lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_kvcache_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kcache), _ptr(vcache),
+                                     _ptr(cache_seqlens), _ptr(o), _ptr(lse), int(bool(causal)), S, B, Nq, Hq, Hkv,
+                                     cap, d, float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache_append")
+    return o, lse
+
+
+def fa_fwd_kvcache_paged_append(q, kpages, vpages, block_table, cache_seqlens, k_new=None, v_new=None, causal=True,
+                                o=None, lse=None, num_splits=None, scale=None, workspace=None, stream=None,
+                                want_lse=True):
+    """``fa_fwd_kvcache_append`` over a paged cache (``fa_fwd_kvcache_paged_append``).
+
+    kpages, vpages: (num_pages, page_size, Hkv, d) bf16; block_table:
+    (B, pages_per_seq) int32. Returns (o (B, Nq, Hq, d), lse (B, Hq, Nq)).
+    """
+    import torch
+    num_pages, page_size, Hkv, d = kpages.shape
+    if tuple(vpages.shape) != tuple(kpages.shape):
+        raise ValueError("page pool shapes do not match")
+    for t, n in ((kpages, "kpages"), (vpages, "vpages")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(block_table, "block_table", torch.int32, q.device)
+    if block_table.dim() != 2 or block_table.shape[0] != q.shape[0]:
+        raise ValueError("block_table must be (B, pages_per_seq)")
+    pages_per_seq = block_table.shape[1]
+    B, Nq, Hq, o, lse, S, workspace, ws_bytes = _append_common(q, k_new, v_new, cache_seqlens, Hkv, d,
+                                                                page_size * pages_per_seq, o, lse, num_splits,
+                                                                workspace, want_lse)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_kvcache_paged_append(_ptr(q), _ptr(k_new), _ptr(v_new), _ptr(kpages), _ptr(vpages),
+                                           _ptr(block_table), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
+                                           int(bool(causal)), S, B, Nq, Hq, Hkv, page_size, pages_per_seq, num_pages,
+                                           d, float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache_paged_append")
     return o, lse
 
 

@@ -181,20 +181,22 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs
 
 namespace {
 
-fa_status_t kvcache(const void* q, const void* kcache, const void* vcache, const int32_t* block_table,
-                    int page_size, int pages_per_seq, int num_pages,
-                    const int32_t* cache_seqlens, void* o, float* lse,
-                    int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+fa_status_t kvcache(const void* q, const void* k_new, const void* v_new, const void* kcache, const void* vcache,
+                    const int32_t* block_table, int page_size, int pages_per_seq, int num_pages,
+                    const int32_t* cache_seqlens, void* o, float* lse, int causal,
+                    int num_splits, int B, int Nq, int Hq, int Hkv, int capacity, int d,
                     float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+  if (B < 0 || Nq < 1 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if ((k_new == nullptr) != (v_new == nullptr)) return FA_ERR_INVALID_ARG;
   if (!fa::decode_supported(d, Hq / Hkv)) return FA_ERR_UNSUPPORTED;
   if (num_splits > 65535 || Hkv > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq * Hq > 0x7fffffff || (int64_t)Nq * Hq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   if (B == 0) return FA_OK;
   if (q == nullptr || o == nullptr || cache_seqlens == nullptr) return FA_ERR_INVALID_ARG;
   if (capacity > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_INVALID_ARG;
-  const size_t need = fa::decode_workspace_bytes(B, Hq, d, num_splits);
+  const size_t need = fa::decode_workspace_bytes(B * Nq, Hq, d, num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
 
   fa::DecodeArgs a;
@@ -216,6 +218,10 @@ fa_status_t kvcache(const void* q, const void* kcache, const void* vcache, const
   a.page_size = page_size;
   a.pages_per_seq = pages_per_seq;
   a.num_pages = num_pages;
+  a.Nq = Nq;
+  a.causal = causal != 0;
+  a.k_new = k_new;
+  a.v_new = v_new;
   return launch_status(fa::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -225,8 +231,16 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
                            const int32_t* cache_seqlens, void* o, float* lse,
                            int num_splits, int B, int Hq, int Hkv, int capacity, int d,
                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
-  return kvcache(q, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, num_splits, B, Hq, Hkv, capacity, d,
-                 scale, workspace, workspace_bytes, stream);
+  return kvcache(q, nullptr, nullptr, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, 0, num_splits, B, 1,
+                 Hq, Hkv, capacity, d, scale, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_fwd_kvcache_append(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                                  const int32_t* cache_seqlens, void* o, float* lse, int causal, int num_splits,
+                                  int B, int Nq, int Hq, int Hkv, int capacity, int d, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  return kvcache(q, k_new, v_new, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, causal, num_splits, B, Nq,
+                 Hq, Hkv, capacity, d, scale, workspace, workspace_bytes, stream);
 }
 
 fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* vpages,
@@ -238,8 +252,23 @@ fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* 
     return FA_ERR_INVALID_ARG;
   if ((int64_t)page_size * pages_per_seq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   if (B > 0 && block_table == nullptr) return FA_ERR_INVALID_ARG;
-  return kvcache(q, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens, o, lse,
-                 num_splits, B, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace, workspace_bytes, stream);
+  return kvcache(q, nullptr, nullptr, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens,
+                 o, lse, 0, num_splits, B, 1, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace,
+                 workspace_bytes, stream);
+}
+
+fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const void* v_new, void* kpages,
+                                        void* vpages, const int32_t* block_table, const int32_t* cache_seqlens,
+                                        void* o, float* lse, int causal, int num_splits, int B, int Nq, int Hq,
+                                        int Hkv, int page_size, int pages_per_seq, int num_pages, int d, float scale,
+                                        void* workspace, size_t workspace_bytes, void* stream) {
+  if (page_size <= 0 || page_size % fa::kDecodePageAlign != 0 || pages_per_seq <= 0 || num_pages <= 0)
+    return FA_ERR_INVALID_ARG;
+  if ((int64_t)page_size * pages_per_seq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && block_table == nullptr) return FA_ERR_INVALID_ARG;
+  return kvcache(q, k_new, v_new, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens, o,
+                 lse, causal, num_splits, B, Nq, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace,
+                 workspace_bytes, stream);
 }
 
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {

@@ -36,16 +36,25 @@ constexpr int kMaxGroup = 16;    // query heads per key/value head (MFMA columns
 constexpr float kSlack = 8.f;
 
 struct DecParams {
-  const char* __restrict__ q;
-  const char* __restrict__ kc;
-  const char* __restrict__ vc;
+  const char* __restrict__ q;  // (B, Nq, Hq, D)
+  char* __restrict__ kc;       // written only by the append
+  char* __restrict__ vc;
   const int32_t* __restrict__ lens;
-  char* __restrict__ o;
-  float* __restrict__ lse;
-  float* __restrict__ part_o;    // (B, Hq, S, D)
-  float* __restrict__ part_lse;  // (B, Hq, S), base-2 units
+  char* __restrict__ o;          // (B, Nq, Hq, D)
+  float* __restrict__ lse;       // (B, Hq, Nq)
+  float* __restrict__ part_o;    // (B, Nq, Hq, S, D)
+  float* __restrict__ part_lse;  // (B, Nq, Hq, S), base-2 units
   int Hq, Hkv, group, capacity, S, chunk;
   float c;  // scale * log2(e)
+  // Nq queries per sequence, served as ncg groups of 16 (query, head)
+  // columns; query i of sequence b is bottom-right aligned: with n = its
+  // cache length plus n_new, it sees keys j <= n - Nq + i when causal
+  int Nq, ncg, causal;
+  // rows appended per sequence (0 or Nq): k_new / v_new (B, Nq, Hkv, D)
+  // are written at rows lens[b] .. lens[b] + Nq - 1 before they are read
+  int n_new;
+  const char* __restrict__ kn;
+  const char* __restrict__ vn;
   // paged cache (block_table non-null): sequence b's keys [i P, (i+1) P)
   // sit in page block_table[b * pages_per_seq + i] of kc / vc, each page
   // P = page_size rows of (Hkv, D); indices are clamped to [0, num_pages)
@@ -53,8 +62,23 @@ struct DecParams {
   int page_size, pages_per_seq, num_pages;
 };
 
-__device__ __forceinline__ int seq_len(const DecParams& p, int b) {
+// Rows held before this call, clamped to [0, capacity].
+__device__ __forceinline__ int base_len(const DecParams& p, int b) {
   return min(max(p.lens[b], 0), p.capacity);
+}
+
+// Rows attended: the held ones plus the appended ones, within capacity.
+__device__ __forceinline__ int seq_len(const DecParams& p, int b) {
+  return min(base_len(p, b) + p.n_new, p.capacity);
+}
+
+// Row of the (B * capacity or num_pages * page_size, Hkv, D) cache array
+// that holds key `key` of sequence b.
+__device__ __forceinline__ int64_t cache_row(const DecParams& p, int b, int key) {
+  if (p.block_table == nullptr) return (int64_t)b * p.capacity + key;
+  const int slot = key / p.page_size;
+  const int page = min(max(p.block_table[(int64_t)b * p.pages_per_seq + slot], 0), p.num_pages - 1);
+  return (int64_t)page * p.page_size + (key - slot * p.page_size);
 }
 
 // Tile shape: T keys per tile (a multiple of the 32-key MFMA step) and an
@@ -81,14 +105,16 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
 
   const int lane = threadIdx.x;
-  const int col = lane & 15;  // query head within the group (MFMA column)
+  const int col = lane & 15;  // MFMA column: one (query, query head) pair
   const int g4 = lane >> 4;   // lane quarter
   // The Hkv heads of one (sequence, split) are adjacent in dispatch order,
   // so together they stream whole contiguous cache rows. Splits go in
   // decreasing index: the last splits exist only for the longest sequences
   // (or are empty and exit at once), so the tail of the launch is made of
   // split 0 .. 1 workgroups, present and full-length for every sequence.
-  const int h = blockIdx.x, b = blockIdx.y, s = p.S - 1 - (int)blockIdx.z;
+  const int h = (int)blockIdx.x / p.ncg, cg = (int)blockIdx.x - h * p.ncg;
+  const int b = blockIdx.y, s = p.S - 1 - (int)blockIdx.z;
+  const int base = base_len(p, b);
   const int L = seq_len(p, b);
   const int start = s * p.chunk;
   const int end = min(start + p.chunk, L);
@@ -97,8 +123,35 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
 
   const int G = p.group;
   const int kv_row = p.Hkv * D * 2;  // bytes between cache rows
-  const char* kbase = p.kc + (((int64_t)b * p.capacity + start) * p.Hkv + h) * D * 2;
-  const char* vbase = p.vc + (((int64_t)b * p.capacity + start) * p.Hkv + h) * D * 2;
+
+  // Append: this split's share [max(start, base), end) of the new rows goes
+  // into the cache before any of it is read back. Every column group of
+  // the split writes the same bytes; each reads only after its own writes
+  // have completed, so all of them see the new rows.
+  if (p.n_new > 0 && end > max(start, base)) {
+    const int r0 = max(start, base);
+    for (int idx = lane; idx < (end - r0) * TL::CPR; idx += 64) {
+      const int r = r0 + idx / TL::CPR, cc = idx % TL::CPR;
+      const int64_t src = (((int64_t)b * p.Nq + (r - base)) * p.Hkv + h) * D * 2 + cc * 16;
+      const int64_t dst = (cache_row(p, b, r) * p.Hkv + h) * D * 2 + cc * 16;
+      *reinterpret_cast<u32x4*>(p.kc + dst) = *reinterpret_cast<const u32x4*>(p.kn + src);
+      *reinterpret_cast<u32x4*>(p.vc + dst) = *reinterpret_cast<const u32x4*>(p.vn + src);
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    wait_vm_loads();
+  }
+
+  // Column col of group cg: query qi = c / G, head g = c % G (c = 16 cg + col).
+  // Its last visible key, relative to the split start, bounds the mask.
+  const int cidx = 16 * cg + col;
+  const bool cvalid = cidx < p.Nq * G;
+  const int qi = cvalid ? cidx / G : p.Nq - 1;
+  const int n_all = base + p.n_new;  // causal alignment point (may pass capacity)
+  const int climit = (p.causal ? min(end - 1, n_all - p.Nq + qi) : end - 1) - start;
+  // tiles whose every key is visible to every column of the group
+  const int first_q = min(16 * cg / G, p.Nq - 1);
+  const int gmin = (p.causal ? min(end - 1, n_all - p.Nq + first_q) : end - 1) - start;
+  const int nfull = max(gmin + 1, 0) / T;
 
   // DMA addressing: load j of a tile fills slot 64 j + lane (row slot / CPR)
   int dma_row[TL::DMA], dma_col[TL::DMA];
@@ -111,18 +164,11 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   auto issue_tile = [&](int t) {
     const int j0 = t * T;
     const int last = end - start - 1 - j0;  // rows past the end re-read the last key (masked later)
-    const char* ks = kbase + (int64_t)j0 * kv_row;
-    const char* vs = vbase + (int64_t)j0 * kv_row;
-    if (p.block_table != nullptr) {
-      // a tile never straddles pages: page_size and the split starts are
-      // multiples of the 64-key split alignment, tiles divide it
-      const int key = start + j0;
-      const int slot = key / p.page_size;
-      const int page = min(max(p.block_table[(int64_t)b * p.pages_per_seq + slot], 0), p.num_pages - 1);
-      const int64_t row = (int64_t)page * p.page_size + (key - slot * p.page_size);
-      ks = p.kc + (row * p.Hkv + h) * D * 2;
-      vs = p.vc + (row * p.Hkv + h) * D * 2;
-    }
+    // a tile never straddles pages: page_size and the split starts are
+    // multiples of the 64-key split alignment, tiles divide it
+    const int64_t row = cache_row(p, b, start + j0);
+    const char* ks = p.kc + (row * p.Hkv + h) * D * 2;
+    const char* vs = p.vc + (row * p.Hkv + h) * D * 2;
     const uint32_t st = lds0 + (uint32_t)((t % NST) * TL::STAGE);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
@@ -135,13 +181,15 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   for (int t = 0; t < NST - 1; ++t)
     if (t < ntiles) issue_tile(t);
 
-  // Q^T as B operand of 16x16x32: register i of k-step ks = Q[h G + col][32 ks + 8 g4 + i]
+  // Q^T as B operand of 16x16x32: register i of k-step ks = Q[qi][h G + g][32 ks + 8 g4 + i]
+  const int hq = h * G + (cvalid ? cidx - qi * G : 0);
+  const int64_t orow = ((int64_t)b * p.Nq + qi) * p.Hq + hq;  // row of o and of the partials
   bf16x8 qf[D / 32];
   {
-    const char* qrow = p.q + ((int64_t)b * p.Hq + h * G + col) * D * 2;
+    const char* qrow = p.q + orow * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 32; ++ks)
-      qf[ks] = col < G ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 32 + g4 * 8) * 2) : bf16x8{};
+      qf[ks] = cvalid ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 32 + g4 * 8) * 2) : bf16x8{};
   }
   wait_vm_loads();
 
@@ -181,7 +229,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
       }
     }
     if constexpr (MASK) {
-      const int lim = end - start - 1 - t * T - 4 * g4;  // key offset 16 tb + i visible iff <= lim
+      const int lim = climit - t * T - 4 * g4;  // key offset 16 tb + i visible iff <= lim
 #pragma unroll
       for (int tb = 0; tb < T / 16; ++tb)
 #pragma unroll
@@ -249,8 +297,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   };
 
   int t = 0;
-  const int nfull = (end - start) / T;  // tiles with every key valid
-  for (; t < nfull; ++t) {
+  for (; t < min(nfull, ntiles); ++t) {
     if (t + NST - 1 < ntiles) issue_tile(t + NST - 1);
     wait_tile(t);
     compute_tile(t, std::false_type{});
@@ -263,9 +310,9 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
 
   // epilogue: sum l over the lane quarters, normalise, write
   l = quarters_sum(l);
-  if (col < G) {
+  if (cvalid) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    const int64_t row = (int64_t)b * p.Hq + h * G + col;
+    const int64_t row = orow;
     if (p.S == 1) {
 #pragma unroll
       for (int dt = 0; dt < D / 16; ++dt) {
@@ -274,7 +321,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
         w[1] = pack_bf16x2(acc[dt][2] * inv, acc[dt][3] * inv);
         *reinterpret_cast<u32x2*>(p.o + (row * D + dt * 16 + 4 * g4) * 2) = w;
       }
-      if (g4 == 0 && p.lse != nullptr) p.lse[row] = l > 0.f ? (m + log2_fast(l)) * kLn2 : -INFINITY;
+      if (g4 == 0 && p.lse != nullptr)
+        p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = l > 0.f ? (m + log2_fast(l)) * kLn2 : -INFINITY;
     } else {
       float* po = p.part_o + (row * p.S + s) * D;
 #pragma unroll
@@ -290,9 +338,10 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
 template <int D>
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int rows) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b * Nq + i) * Hq + hq
   if (row >= rows) return;
-  const int b = row / p.Hq;
+  const int bi = row / p.Hq, hq = row - bi * p.Hq;
+  const int b = bi / p.Nq, qi = bi - b * p.Nq;
   const int L = seq_len(p, b);
   const int n = (L + p.chunk - 1) / p.chunk;  // splits that hold keys
   const float* pl = p.part_lse + (int64_t)row * p.S;
@@ -314,15 +363,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int ro
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) reinterpret_cast<bf16*>(p.o)[(int64_t)row * D + lane * PER + e] = (bf16)(o[e] * inv);
-  if (lane == 0 && p.lse != nullptr) p.lse[row] = wsum > 0.f ? (Mu + log2_fast(wsum)) * kLn2 : -INFINITY;
+  if (lane == 0 && p.lse != nullptr)
+    p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = wsum > 0.f ? (Mu + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
 template <int D, class TL>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   DecParams p;
   p.q = static_cast<const char*>(a.q);
-  p.kc = static_cast<const char*>(a.kcache);
-  p.vc = static_cast<const char*>(a.vcache);
+  p.kc = static_cast<char*>(const_cast<void*>(a.kcache));
+  p.vc = static_cast<char*>(const_cast<void*>(a.vcache));
   p.lens = a.seqlens;
   p.o = static_cast<char*>(a.o);
   p.lse = a.lse;
@@ -339,15 +389,21 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   p.page_size = a.page_size;
   p.pages_per_seq = a.pages_per_seq;
   p.num_pages = a.num_pages;
+  p.Nq = a.Nq;
+  p.ncg = (a.Nq * p.group + 15) / 16;
+  p.causal = a.causal;
+  p.n_new = a.k_new != nullptr ? a.Nq : 0;
+  p.kn = static_cast<const char*>(a.k_new);
+  p.vn = static_cast<const char*>(a.v_new);
   if (p.S > 1) {
     p.part_o = static_cast<float*>(a.workspace);
-    p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;
+    p.part_lse = p.part_o + (size_t)a.B * a.Nq * a.Hq * p.S * D;
   }
-  dim3 grid(a.Hkv, a.B, p.S);
+  dim3 grid(a.Hkv * p.ncg, a.B, p.S);
   hipLaunchKernelGGL((decode_split_kernel<D, TL>), grid, dim3(64), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.S == 1) return e;
-  const int rows = a.B * a.Hq;
+  const int rows = a.B * a.Nq * a.Hq;
   hipLaunchKernelGGL((decode_combine_kernel<D>), dim3((rows + 3) / 4), dim3(256), 0, stream, p, rows);
   return hipGetLastError();
 }

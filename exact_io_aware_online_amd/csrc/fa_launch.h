@@ -45,6 +45,14 @@ struct DecodeArgs {
   // paged cache: null for a contiguous (B, capacity, Hkv, d) cache
   const int32_t* block_table = nullptr;
   int page_size = 0, pages_per_seq = 0, num_pages = 0;
+  // Nq queries per sequence (q, o: (B, Nq, Hq, d); lse: (B, Hq, Nq)),
+  // bottom-right causal when `causal`; k_new / v_new (B, Nq, Hkv, d), when
+  // non-null, are written into the cache at rows seqlens[b] .. + Nq - 1
+  // and attended
+  int Nq = 1;
+  int causal = 0;
+  const void* k_new = nullptr;
+  const void* v_new = nullptr;
 };
 
 struct BwdArgs {

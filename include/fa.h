@@ -183,6 +183,45 @@ fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* 
                                  int num_pages, int d, float scale, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/* Decode step that appends to the cache in the same launch (pyshine.com
+ * FlashAttention code tour, "Why You Need This" and its usage example: the
+ * with-kvcache entry point updates the preallocated cache in place with the
+ * new tokens, then attends; causal masking is bottom-right aligned since
+ * version 2.1). Nq >= 1 queries per sequence:
+ *   q, o           : (B, Nq, Hq, d) bfloat16    lse : (B, Hq, Nq) float32 or NULL
+ *   k_new, v_new   : (B, Nq, Hkv, d) bfloat16, both NULL (attend to the
+ *                    cache as it is) or both set (append first)
+ *   kcache, vcache : (B, capacity, Hkv, d) bfloat16; with k_new set, rows
+ *                    base_b .. base_b + Nq - 1 are overwritten, where base_b
+ *                    is cache_seqlens[b] clamped to [0, capacity]; rows at or
+ *                    past capacity are dropped. No other row is written.
+ *   cache_seqlens  : (B,) int32 on the device, read only (the caller
+ *                    advances it after the step)
+ * With n_b = base_b + (Nq if appending else 0), query i of sequence b sees
+ * keys j < min(n_b, capacity) and, when causal, only j <= n_b - Nq + i; a
+ * query that sees no key gets o = 0 and lse = -inf.
+ * Splits, workspace and stream rules are those of fa_fwd_kvcache with B * Nq
+ * in place of B in fa_fwd_kvcache_workspace_size. The new rows must not
+ * alias q, o or one another. Calls that write one cache must be ordered on
+ * one stream. With Nq = 1 and nothing appended the results are bitwise
+ * those of fa_fwd_kvcache. Nq * (Hq / Hkv) (query, head) pairs per key/value
+ * head are served 16 per workgroup; each such group streams the cache once.
+ * FA_ERR_INVALID_ARG for Nq < 1 or only one of k_new / v_new. */
+fa_status_t fa_fwd_kvcache_append(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
+                                  const int32_t* cache_seqlens, void* o, float* lse, int causal, int num_splits,
+                                  int B, int Nq, int Hq, int Hkv, int capacity, int d, float scale,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_fwd_kvcache_append over a paged cache: the pages and block_table are
+ * those of fa_fwd_kvcache_paged (capacity = page_size * pages_per_seq), the
+ * new rows land in the pages that block_table names for positions base_b ..
+ * base_b + Nq - 1. */
+fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const void* v_new, void* kpages,
+                                        void* vpages, const int32_t* block_table, const int32_t* cache_seqlens,
+                                        void* o, float* lse, int causal, int num_splits, int B, int Nq, int Hq,
+                                        int Hkv, int page_size, int pages_per_seq, int num_pages, int d, float scale,
+                                        void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of device workspace fa_bwd needs: two float32 values (D_i and
  * -LSE_i / scale) per (batch, query head, query), the query count rounded
  * up to a multiple of 32. 0 when B, Hq or Nq is not positive. */

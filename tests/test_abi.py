@@ -149,3 +149,32 @@ def test_backward_host_validation():
     assert call(B=0) == fa.FA_OK
     assert fa.fa_bwd_workspace_size(2, 3, 33) == 2 * 2 * 3 * 64 * 4
     assert fa.fa_bwd_workspace_size(2, 3, 0) == 0
+
+
+def test_append_host_validation():
+    import ctypes
+    L = fa.lib()
+    null = None
+    fake = ctypes.c_void_p(64)  # never dereferenced: every case fails or ends before a launch
+    def call(q=fake, kn=null, vn=null, o=fake, lens=fake, causal=1, S=1, B=2, Nq=3, Hq=8, Hkv=2, cap=256, d=128,
+             ws=null, ws_bytes=0):
+        return L.fa_fwd_kvcache_append(q, kn, vn, fake, fake, lens, o, null, causal, S, B, Nq, Hq, Hkv, cap, d, 0.1,
+                                       ws, ws_bytes, null)
+    assert call(Nq=0) == fa.FA_ERR_INVALID_ARG
+    assert call(kn=fake) == fa.FA_ERR_INVALID_ARG          # k_new without v_new
+    assert call(vn=fake) == fa.FA_ERR_INVALID_ARG
+    assert call(Hq=6, Hkv=4) == fa.FA_ERR_INVALID_ARG      # Hq % Hkv
+    assert call(Hq=64, Hkv=2) == fa.FA_ERR_UNSUPPORTED     # more than 16 query heads per key/value head
+    assert call(B=40000, Nq=40000) == fa.FA_ERR_UNSUPPORTED
+    assert call(q=null) == fa.FA_ERR_INVALID_ARG
+    assert call(S=2) == fa.FA_ERR_WORKSPACE                 # splits need the (B * Nq)-row workspace
+    need = fa.fa_fwd_kvcache_workspace_size(2 * 3, 8, 128, 2)
+    assert need == 2 * 3 * 8 * 2 * 129 * 4
+    assert call(S=2, ws=fake, ws_bytes=need - 1) == fa.FA_ERR_WORKSPACE
+    assert call(B=0, q=null, o=null, lens=null) == fa.FA_OK
+    # paged: page size not a multiple of 64, missing block table
+    def paged(page=128, bt=fake):
+        return L.fa_fwd_kvcache_paged_append(fake, null, null, fake, fake, bt, fake, fake, null, 1, 1, 2, 3, 8, 2,
+                                             page, 4, 16, 128, 0.1, null, 0, null)
+    assert paged(page=96) == fa.FA_ERR_INVALID_ARG
+    assert paged(bt=null) == fa.FA_ERR_INVALID_ARG
