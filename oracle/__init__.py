@@ -11,6 +11,7 @@ definition down (FlashAttention: Part 2, section 6.2 "FlashAttention
 Summary": ordinary attention forms Q K^T as an N x N matrix).
 """
 
+from . import fp8  # noqa: F401
 from . import sdpa  # noqa: F401
 from .sdpa import (  # noqa: F401
     kv_head_of,

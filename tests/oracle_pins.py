@@ -18,6 +18,7 @@ import os
 
 import numpy as np
 
+from oracle import fp8 as F8
 from oracle import sdpa as O
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -503,6 +504,172 @@ def pin_decode_append_capacity_overflow(tol=1e-12):
     assert np.max(np.abs(o - ob)) <= tol and np.max(np.abs(l - lb)) <= tol
 
 
+# ---------------------------------------------------------------------------
+# FP8: e4m3 codes, the randomised Hadamard rotation, block quantisation and
+# attention on quantised operands
+# ---------------------------------------------------------------------------
+def _torch_e4m3(x):
+    import torch
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_against_torch(tol=0.0):
+    """Encoding and decoding agree with torch's float8_e4m3fn cast on every
+    code, every midpoint between neighbours and random values."""
+    import torch
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = F8.e4m3_decode(codes)
+    assert np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(got[~np.isnan(got)], ref[~np.isnan(ref)])
+    fin = np.unique(np.abs(ref[np.isfinite(ref)]))
+    mids = (fin[1:] + fin[:-1]) / 2
+    r = np.random.default_rng(2400)
+    x = np.concatenate([fin, -fin, mids, -mids, r.normal(size=4000) * 40,
+                        r.uniform(-1, 1, 4000) * 2.0 ** r.integers(-12, 8, 4000)])
+    x = np.clip(x, -448, 448).astype(np.float32).astype(np.float64)  # exact in float32 for torch
+    assert np.array_equal(F8.e4m3_encode(x), _torch_e4m3(x)), "e4m3 encoding"
+
+
+def pin_hadamard_rotation(tol=1e-12):
+    """H_d equals scipy's Hadamard matrix; R = H diag(s) / sqrt(d) is
+    orthogonal, so rotating Q and K keeps every score."""
+    import scipy.linalg
+    for d in (1, 2, 8, 64, 128):
+        assert np.array_equal(F8.hadamard(d), scipy.linalg.hadamard(d))
+    r = np.random.default_rng(2410)
+    d = 64
+    s = r.choice([-1.0, 1.0], size=d)
+    R = F8.rotate(np.eye(d), s).T
+    assert np.max(np.abs(R @ R.T - np.eye(d))) <= tol
+    q, k = r.normal(size=(5, d)), r.normal(size=(7, d))
+    assert np.max(np.abs(F8.rotate(q, s) @ F8.rotate(k, s).T - q @ k.T)) <= 1e-11
+    # sign flips act before the transform: rotating the unit vector e_i gives
+    # s_i times column i of scipy's H, over sqrt(d)
+    Hs = scipy.linalg.hadamard(d)
+    for i in range(d):
+        ei = np.zeros(d)
+        ei[i] = 1.0
+        assert np.max(np.abs(F8.rotate(ei, s) - s[i] * Hs[:, i] / 8.0)) <= tol, ("rotation column", i)
+
+
+def pin_block_exponent(tol=0.0):
+    """Closed forms and the defining inequality amax <= 448 2^e < 2 amax."""
+    cases = {448.0: 0, 449.0: 1, 224.0: -1, 224.5: 0, 1.0: -8, 0.0: 0, 448.0 * 2.0 ** 40: 40,
+             2.0 ** -200: -127, 1e30: 91}
+    for a, e in cases.items():
+        assert F8.block_exponent(a) == e, (a, F8.block_exponent(a), e)
+    r = np.random.default_rng(2420)
+    for a in np.abs(r.normal(size=500)) * 2.0 ** r.integers(-60, 60, 500):
+        e = F8.block_exponent(float(a))
+        assert a <= 448.0 * 2.0 ** e and a > 448.0 * 2.0 ** (e - 1)
+
+
+def pin_quantize_rows(tol=0.0):
+    """Codes round each value to the nearest multiple the block's scale
+    allows (half an e4m3 step), padding rows are zero, and scaling one block
+    by a power of two moves only its exponent."""
+    r = np.random.default_rng(2430)
+    x = r.normal(size=(150, 16)) * 3.0
+    x[70:128] *= 1000.0
+    codes, exps = F8.quantize_rows(x)
+    assert codes.shape == (192, 16) and exps.shape == (3,)
+    assert not codes[150:].any()
+    xh = F8.e4m3_decode(codes) * np.repeat(2.0 ** exps, 64)[:, None]
+    for blk in range(3):
+        rows = slice(64 * blk, min(64 * blk + 64, 150))
+        amax = np.max(np.abs(x[rows]))
+        assert amax <= 448.0 * 2.0 ** exps[blk] < 2 * amax
+        step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(x[rows]), 1e-300))) - 3),
+                          2.0 ** (exps[blk] - 9))
+        assert np.all(np.abs(xh[rows] - x[rows]) <= step / 2 * (1 + 1e-12))
+    y = x.copy()
+    y[64:128] *= 2.0 ** 5
+    c2, e2 = F8.quantize_rows(y)
+    assert np.array_equal(c2, codes) and list(e2 - exps) == [0, 5, 0]
+
+
+def _fp8_case(seed, B, Nq, Nk, Hq, Hkv, d, integer_scores=False):
+    r = np.random.default_rng(seed)
+    q = r.normal(size=(B, Nq, Hq, d))
+    k = r.normal(size=(B, Nk, Hkv, d))
+    v = r.normal(size=(B, Nk, Hkv, d))
+    if integer_scores:  # every score an integer: q rows one-hot times small integers, k small integers
+        q = np.zeros((B, Nq, Hq, d))
+        q[..., 0] = 1.0
+        k = r.integers(-6, 4, size=(B, Nk, Hkv, d)).astype(np.float64)
+    qc, qe = F8.quantize_bhnd(q)
+    kc, ke = F8.quantize_bhnd(k)
+    vc, ve = F8.quantize_bhnd(v)
+    return qc, qe, kc, ke, vc, ve
+
+
+def pin_attention_fp8_exact_probabilities(tol=1e-12):
+    """When every score (in base-2 units) is an integer, each quantised
+    probability 2^(t - M + 6) is exactly an e4m3 value, so the FP8 model
+    equals exact attention on the dequantised operands."""
+    B, Nq, Nk, Hq, Hkv, d = 1, 70, 70, 4, 2, 8
+    qc, qe, kc, ke, vc, ve = _fp8_case(2440, B, Nq, Nk, Hq, Hkv, d, integer_scores=True)
+    scale = 1.0 / math.log2(math.e)  # t = q . k exactly up to one rounding of the product
+    deq = lambda c, e, n: np.transpose(F8.dequantize_bhnd(c, e)[:, :, :n], (0, 2, 1, 3))
+    for causal in (False, True):
+        o, l = F8.attention_fp8(qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale)
+        oe, le = brute_attention(deq(qc, qe, Nq), deq(kc, ke, Nk), deq(vc, ve, Nk), causal, scale)
+        assert np.max(np.abs(o - oe)) <= tol, ("fp8 exact probabilities O", causal)
+        assert np.max(np.abs(l - le)) <= tol, ("fp8 exact probabilities LSE", causal)
+
+
+def pin_attention_fp8_error_bound(tol=1e-12):
+    """On random operands the FP8 model stays within the bound its
+    probability rounding allows around exact attention on the dequantised
+    operands: |dO| <= (2^-4 sum_j p_j |v_j| + 2^-16 sum_j |v_j|) / sum_j p_j
+    (relative half-step of a normal e4m3 value, half a subnormal step), and
+    its LSE is the exact one (the denominator is not quantised)."""
+    B, Nq, Nk, Hq, Hkv, d = 1, 90, 130, 2, 1, 16
+    qc, qe, kc, ke, vc, ve = _fp8_case(2450, B, Nq, Nk, Hq, Hkv, d)
+    scale = 0.3
+    o, l = F8.attention_fp8(qc, qe, kc, ke, vc, ve, Nq, Nk, False, scale)
+    Q = F8.dequantize_bhnd(qc, qe)[0, :, :Nq]
+    K = F8.dequantize_bhnd(kc, ke)[0, :, :Nk]
+    V = F8.dequantize_bhnd(vc, ve)[0, :, :Nk]
+    worst = 0.0
+    for h in range(Hq):
+        s = scale * Q[h] @ K[0].T
+        p = np.exp(s - s.max(axis=1, keepdims=True))
+        oe = p @ V[0] / p.sum(axis=1, keepdims=True)
+        le = np.log(p.sum(axis=1)) + s.max(axis=1)
+        bound = (2.0 ** -4 * p @ np.abs(V[0]) + 2.0 ** -16 * np.abs(V[0]).sum(axis=0)[None, :]) / p.sum(axis=1)[:, None]
+        err = np.abs(o[0, :, h] - oe)
+        assert np.all(err <= bound * (1 + 1e-9)), "fp8 error bound"
+        assert np.max(np.abs(l[0, h] - le)) <= tol, "fp8 LSE"
+        worst = max(worst, float(np.max(err)))
+    assert worst > 0.0  # the probabilities really were rounded
+
+
+def pin_attention_fp8_brute_force(tol=1e-12):
+    """Plain loops with torch's e4m3 cast for the probabilities."""
+    B, Nq, Nk, Hq, Hkv, d = 1, 5, 7, 2, 1, 4
+    qc, qe, kc, ke, vc, ve = _fp8_case(2460, B, Nq, Nk, Hq, Hkv, d)
+    scale = 0.7
+    Q = F8.dequantize_bhnd(qc, qe)
+    K = F8.dequantize_bhnd(kc, ke)
+    V = F8.dequantize_bhnd(vc, ve)
+    import torch
+    for causal in (False, True):
+        o, l = F8.attention_fp8(qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale)
+        for h in range(Hq):
+            for i in range(Nq):
+                keys = [j for j in range(Nk) if not causal or j <= i]
+                t = [scale / math.log(2.0) * math.fsum(Q[0, h, i, x] * K[0, 0, j, x] for x in range(d)) for j in keys]
+                M = math.ceil(max(t))
+                den = math.fsum(2.0 ** (x - M) for x in t)
+                pq = [float(torch.tensor(2.0 ** (x - M + 6), dtype=torch.float32).to(torch.float8_e4m3fn).float())
+                      for x in t]
+                for x in range(d):
+                    want = 2.0 ** -6 * math.fsum(pq[n] * V[0, 0, j, x] for n, j in enumerate(keys)) / den
+                    assert abs(o[0, i, h, x] - want) <= tol, ("fp8 brute O", causal, h, i, x)
+                assert abs(l[0, h, i] - math.log(2.0) * (M + math.log2(den))) <= tol, ("fp8 brute LSE", causal)
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -532,4 +699,11 @@ ALL_PINS = [
     pin_decode_append_cache_update,
     pin_decode_append_reduces_to_decode,
     pin_decode_append_capacity_overflow,
+    pin_e4m3_against_torch,
+    pin_hadamard_rotation,
+    pin_block_exponent,
+    pin_quantize_rows,
+    pin_attention_fp8_exact_probabilities,
+    pin_attention_fp8_error_bound,
+    pin_attention_fp8_brute_force,
 ]

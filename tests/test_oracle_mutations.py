@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 
 import oracle_pins as P
+from oracle import fp8 as F8
 from oracle import sdpa as O
 
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
@@ -234,6 +235,98 @@ MUTATIONS = [
     ("decode_append", _append_variant("old_length")),
     ("decode_append", _append_variant("top_left")),
 ]
+
+
+_orig_fp8 = {n: getattr(F8, n) for n in ("e4m3_encode", "block_exponent", "rotate", "attention_fp8",
+                                          "dequantize_bhnd", "quantize_rows")}
+
+
+def _e4m3_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    vals = F8.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    idx = np.searchsorted(vals, np.abs(x), side="right") - 1
+    code = idx.astype(np.uint8)
+    return np.where(np.signbit(x), code | 0x80, code).astype(np.uint8)
+
+
+def _e4m3_ties_away(x):
+    x = np.asarray(x, dtype=np.float64)
+    c = _orig_fp8["e4m3_encode"](x)
+    vals = F8.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    a = np.abs(x)
+    hi = np.clip(np.searchsorted(vals, a), 0, len(vals) - 1)
+    tie = (hi > 0) & (vals[hi] - a == a - vals[np.maximum(hi - 1, 0)])
+    up = np.where(np.signbit(x), hi.astype(np.uint8) | 0x80, hi.astype(np.uint8))
+    return np.where(tie, up, c).astype(np.uint8)
+
+
+def _exponent_plus_one(amax):
+    return min(127, _orig_fp8["block_exponent"](amax) + 1) if amax else 0
+
+
+def _rotate_no_signs(x, signs):
+    return _orig_fp8["rotate"](x, np.ones_like(np.asarray(signs, dtype=np.float64)))
+
+
+def _fp8_unquantised_p(qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale):
+    saved = F8.e4m3_encode
+    F8.e4m3_encode = lambda x: x  # decode(x) then sees values, not codes: give it a float path
+    try:
+        dec = F8.e4m3_decode
+        F8.e4m3_decode = lambda c: np.asarray(c, dtype=np.float64) if np.asarray(c).dtype != np.uint8 else dec(c)
+        return _orig_fp8["attention_fp8"](qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale)
+    finally:
+        F8.e4m3_encode = saved
+        F8.e4m3_decode = dec
+
+
+def _fp8_bias_zero(qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale):
+    saved = F8.P_BIAS
+    F8.P_BIAS = 0
+    try:
+        return _orig_fp8["attention_fp8"](qc, qe, kc, ke, vc, ve, Nq, Nk, causal, scale)
+    finally:
+        F8.P_BIAS = saved
+
+
+def _dequantize_without_exponents(codes, exps):
+    return _orig_fp8["dequantize_bhnd"](codes, np.zeros_like(np.asarray(exps)))
+
+
+def _quantize_rows_32(x):
+    saved = F8.BLOCK
+    F8.BLOCK = 32
+    try:
+        return _orig_fp8["quantize_rows"](x)
+    finally:
+        F8.BLOCK = saved
+
+
+MUTATIONS_FP8 = [
+    ("e4m3_encode", _e4m3_truncate),
+    ("e4m3_encode", _e4m3_ties_away),
+    ("block_exponent", _exponent_plus_one),
+    ("rotate", _rotate_no_signs),
+    ("attention_fp8", _fp8_unquantised_p),
+    ("attention_fp8", _fp8_bias_zero),
+    ("dequantize_bhnd", _dequantize_without_exponents),
+    ("quantize_rows", _quantize_rows_32),
+]
+
+
+@pytest.mark.parametrize("name,bad", MUTATIONS_FP8, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS_FP8])
+def test_some_pin_rejects_fp8_mutation(monkeypatch, name, bad):
+    monkeypatch.setattr(F8, name, bad)
+    failed = []
+    for pin in P.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin()
+        except AssertionError:
+            failed.append(pin.__name__)
+        except Exception as exc:
+            failed.append(f"{pin.__name__}({type(exc).__name__})")
+    assert failed, f"no pin caught the planted mistake {name}:{bad.__name__}"
 
 
 @pytest.mark.parametrize("name,bad", MUTATIONS, ids=[f"{n}:{f.__name__}" for n, f in MUTATIONS])
