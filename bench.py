@@ -9,12 +9,13 @@ timed region. Each launch is bracketed by HIP events on the stream it runs
 on; `value` is the prefill's algorithmic TFLOP/s (4*B*H*Nq*Nk*d, halved for
 causal) over its mean event time, and the decode's algorithmic GB/s is
 reported beside it. After the step loop, and outside its clock, the
-backward, the paged-cache decode and decode steps that append 1 or 4 new
-tokens per sequence are timed on the same workloads. Prints one JSON line.
+backward, the FP8 forward (with its quantisation timed apart), the
+paged-cache decode and decode steps that append 1 or 4 new tokens per
+sequence are timed on the same workloads. Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--prefill NAME]
                     [--no-cpu-baseline] [--splits S] [--bwd-steps N]
-                    [--paged-steps N] [--append-steps N]
+                    [--fp8-steps N] [--paged-steps N] [--append-steps N]
 """
 
 import argparse
@@ -30,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak"
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
+PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 8192 flop/clk x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
 DEFAULT_PREFILL = "mha_bf16_causal_b8_h16_n2048_d128"
 DEFAULT_DECODE = "gqa_bf16_decode_b64_h32kv8_cap8192_d128"
@@ -116,6 +118,9 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--bwd-steps", type=int, default=50,
                     help="timed fa_bwd calls on the prefill workload after the step loop (0 = skip)")
+    ap.add_argument("--fp8-steps", type=int, default=50,
+                    help="timed FP8 forward calls (fa_fwd_fp8 on the prefill workload, quantised with the "
+                         "rotation) after the step loop (0 = skip)")
     ap.add_argument("--append-steps", type=int, default=50,
                     help="timed decode-with-append calls (1 and 4 new tokens per sequence) after the step loop "
                          "(0 = skip)")
@@ -265,6 +270,50 @@ def main():
     # cache (the write happens inside the split kernel), queries bottom-right
     # causal; lengths are capped so the new rows fit. Bytes: the visible
     # cache rows read, the new rows read and written, q, o, lse, lengths.
+    # The prefill workload in FP8: Q and K rotated and block-quantised, V
+    # block-quantised (outside the attention's clock, timed on its own),
+    # then fa_fwd_fp8; its TFLOP/s is priced against the dense FP8 peak.
+    fp8 = None
+    if args.fp8_steps > 0 and wp["dtype"] == "bf16" and wp["d"] == 128 and wp["Nk"] <= 65536:
+        signs = SI.random_signs(wp["d"], seed=wp["seed"] + 4000).to(dev)
+        q8, qs8 = fa.fa_quantize_fp8(q, signs=signs)
+        k8, ks8 = fa.fa_quantize_fp8(k, signs=signs)
+        vt8, vs8 = fa.fa_quantize_fp8(v, transpose=True)
+        o8 = torch.empty_like(q)
+        l8 = torch.empty_like(lse)
+
+        def fstep():
+            fa.fa_fwd_fp8(q8, qs8, k8, ks8, vt8, vs8, wp["Nq"], wp["Nk"], causal=wp["causal"], scale=scale_p,
+                          o=o8, lse=l8)
+
+        def qstep():
+            fa.fa_quantize_fp8(q, signs=signs, codes=q8, scales=qs8)
+            fa.fa_quantize_fp8(k, signs=signs, codes=k8, scales=ks8)
+            fa.fa_quantize_fp8(v, transpose=True, codes=vt8, scales=vs8)
+        for _ in range(max(3, args.fp8_steps // 5)):
+            fstep()
+        torch.cuda.synchronize()
+        fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.fp8_steps)]
+        for e0, e1 in fev:
+            e0.record()
+            fstep()
+            e1.record()
+        torch.cuda.synchronize()
+        f_ms = sum(e0.elapsed_time(e1) for e0, e1 in fev) / len(fev)
+        qev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(10)]
+        for e0, e1 in qev:
+            e0.record()
+            qstep()
+            e1.record()
+        torch.cuda.synchronize()
+        q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / len(qev)
+        f_tf = prefill_flops(wp) / (f_ms * 1e-3) / 1e12
+        fp8 = {"value": round(f_tf, 2), "unit": "TFLOP/s", "kernel": "fwd_fp8_kernel<128>", "dtype": "e4m3",
+               "peak": PEAK_FP8_TFLOPS, "frac": round(f_tf / PEAK_FP8_TFLOPS, 4), "mean_launch_ms": round(f_ms, 5),
+               "quantize_ms": round(q_ms, 5), "steps": args.fp8_steps}
+        del q8, k8, vt8, o8
+
     append = None
     if args.append_steps > 0:
         append = {}
@@ -346,6 +395,7 @@ def main():
             "append": append,
         },
         "backward": bwd,
+        "fp8": fp8,
         "device": {"name": props.name, "cus": props.multi_processor_count,
                    "arch": getattr(props, "gcnArchName", "")},
     }

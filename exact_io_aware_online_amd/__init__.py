@@ -25,6 +25,9 @@ __all__ = [
     "fa_fwd_kvcache_paged",
     "fa_fwd_kvcache_append",
     "fa_fwd_kvcache_paged_append",
+    "fa_fp8_padded_rows",
+    "fa_quantize_fp8",
+    "fa_fwd_fp8",
     "fa_bwd",
     "fa_bwd_workspace_size",
     "FA_DTYPE_BF16",
@@ -78,6 +81,12 @@ def lib():
     L.fa_fwd_kvcache_paged_append.restype = i
     L.fa_fwd_kvcache_paged_append.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f,
                                               vp, sz, vp]
+    L.fa_fp8_padded_rows.restype = i
+    L.fa_fp8_padded_rows.argtypes = [i]
+    L.fa_quantize_fp8.restype = i
+    L.fa_quantize_fp8.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp]
+    L.fa_fwd_fp8.restype = i
+    L.fa_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp]
     L.fa_bwd_workspace_size.restype = sz
     L.fa_bwd_workspace_size.argtypes = [i, i, i]
     L.fa_bwd.restype = i
@@ -416,6 +425,78 @@ def fa_fwd_kvcache_paged_append(q, kpages, vpages, block_table, cache_seqlens, k
                                            d, float(scale), _ptr(workspace), ws_bytes, _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache_paged_append")
+    return o, lse
+
+
+def fa_fp8_padded_rows(n):
+    return int(lib().fa_fp8_padded_rows(int(n)))
+
+
+def fa_quantize_fp8(x, signs=None, transpose=False, codes=None, scales=None, stream=None):
+    """Block quantisation to e4m3 through ``fa_quantize_fp8``.
+
+    x: (B, N, H, d) bf16; signs: (d,) float32 of +-1 (rotation) or None.
+    Returns (codes uint8 (B, H, Np, d), or (B, H, d, Np) when transpose,
+    scales uint8 (B, H, Np / 64)), Np = fa_fp8_padded_rows(N).
+    """
+    import torch
+    if x.dim() != 4:
+        raise ValueError("x must be (batch, seq, heads, head_dim)")
+    B, N, H, d = x.shape
+    _check(x, "x", torch.bfloat16, x.device)
+    if signs is not None:
+        _check(signs, "signs", torch.float32, x.device)
+        if tuple(signs.shape) != (d,):
+            raise ValueError("signs must be (head_dim,)")
+    Np = fa_fp8_padded_rows(N)
+    shape = (B, H, d, Np) if transpose else (B, H, Np, d)
+    if codes is None:
+        codes = torch.empty(shape, dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((B, H, Np // 64), dtype=torch.uint8, device=x.device)
+    _check(codes, "codes", torch.uint8, x.device)
+    _check(scales, "scales", torch.uint8, x.device)
+    if tuple(codes.shape) != shape or tuple(scales.shape) != (B, H, Np // 64):
+        raise ValueError("codes / scales have the wrong shape")
+    st = lib().fa_quantize_fp8(_ptr(x), _ptr(signs), _ptr(codes), _ptr(scales), int(bool(transpose)), B, N, H, d,
+                               _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_quantize_fp8")
+    return codes, scales
+
+
+def fa_fwd_fp8(q8, q_scales, k8, k_scales, vt8, v_scales, Nq, Nk, causal=False, scale=None, o=None, lse=None,
+               stream=None, want_lse=True):
+    """Attention on e4m3 operands through ``fa_fwd_fp8``.
+
+    q8 (B, Hq, Nqp, d), k8 (B, Hkv, Nkp, d), vt8 (B, Hkv, d, Nkp) uint8 codes
+    and their (.., Np / 64) uint8 scales as ``fa_quantize_fp8`` returns
+    them; Nq, Nk the unpadded lengths. Returns (o (B, Nq, Hq, d) bf16,
+    lse (B, Hq, Nq) float32).
+    """
+    import torch
+    B, Hq, Nqp, d = q8.shape
+    Hkv = k8.shape[1]
+    if Nqp != fa_fp8_padded_rows(Nq) or tuple(k8.shape) != (B, Hkv, fa_fp8_padded_rows(Nk), d) \
+            or tuple(vt8.shape) != (B, Hkv, d, fa_fp8_padded_rows(Nk)):
+        raise ValueError("code tensors do not match Nq / Nk")
+    for t, n in ((q8, "q8"), (k8, "k8"), (vt8, "vt8"), (q_scales, "q_scales"), (k_scales, "k_scales"),
+                 (v_scales, "v_scales")):
+        _check(t, n, torch.uint8, q8.device)
+    if o is None:
+        o = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q8.device)
+    _check(o, "o", torch.bfloat16, q8.device)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q8.device)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_fp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(v_scales), _ptr(o),
+                          _ptr(lse), B, Hq, Hkv, int(Nq), int(Nk), d, int(bool(causal)), float(scale),
+                          _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_fp8")
     return o, lse
 
 

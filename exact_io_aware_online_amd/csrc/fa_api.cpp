@@ -271,6 +271,63 @@ fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const 
                  workspace_bytes, stream);
 }
 
+int fa_fp8_padded_rows(int n) { return n <= 0 ? 0 : fa::fp8_padded_rows(n); }
+
+fa_status_t fa_quantize_fp8(const void* x, const float* signs, void* codes, uint8_t* scales, int transpose,
+                            int B, int N, int H, int d, void* stream) {
+  if (B < 0 || N < 0 || H <= 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (transpose != 0 && transpose != 1) return FA_ERR_INVALID_ARG;
+  if (!fa::fp8_quant_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (B > 65535 || H > 65535 || N > 0x7fffffff - 64) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || N == 0) return FA_OK;
+  if (x == nullptr || codes == nullptr || scales == nullptr) return FA_ERR_INVALID_ARG;
+  fa::Fp8QuantArgs a;
+  a.x = x;
+  a.signs = signs;
+  a.codes = codes;
+  a.scales = scales;
+  a.transpose = transpose;
+  a.B = B;
+  a.N = N;
+  a.H = H;
+  a.d = d;
+  return launch_status(fa::launch_quant_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+fa_status_t fa_fwd_fp8(const void* q8, const uint8_t* q_scales, const void* k8, const uint8_t* k_scales,
+                       const void* vt8, const uint8_t* v_scales, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
+  if (!fa::fp8_fwd_supported(d)) return FA_ERR_UNSUPPORTED;
+  if (Nk > fa::kFp8MaxKeys || Nq > 0x7fffffff - 128) return FA_ERR_UNSUPPORTED;
+  if ((((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if (B == 0 || Nq == 0) return FA_OK;
+  if (q8 == nullptr || q_scales == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
+  if (Nk > 0 && (k8 == nullptr || k_scales == nullptr || vt8 == nullptr || v_scales == nullptr))
+    return FA_ERR_INVALID_ARG;
+  fa::Fp8FwdArgs a;
+  a.q8 = q8;
+  a.q_scales = q_scales;
+  a.k8 = k8;
+  a.k_scales = k_scales;
+  a.vt8 = vt8;
+  a.v_scales = v_scales;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.Nq = Nq;
+  a.Nk = Nk;
+  a.d = d;
+  a.causal = causal;
+  a.scale = scale;
+  return launch_status(fa::launch_fwd_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {
   if (B <= 0 || Hq <= 0 || Nq <= 0) return 0;
   return fa::bwd_workspace_bytes(B, Hq, Nq);

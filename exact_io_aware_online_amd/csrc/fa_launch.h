@@ -71,6 +71,38 @@ struct BwdArgs {
   void* workspace;  // >= bwd_workspace_bytes(B, Hq, Nq)
 };
 
+// FP8 (e4m3) forward: a bf16 tensor quantised per 64-row block of one
+// (batch, head), optionally rotated first (signs non-null)
+struct Fp8QuantArgs {
+  const void* x;       // (B, N, H, d) bf16
+  const float* signs;  // (d,) +-1, or null
+  void* codes;         // (B, H, Np, d), or (B, H, d, Np) when transpose
+  uint8_t* scales;     // (B, H, Np / 64) E8M0
+  int transpose;
+  int B, N, H, d;
+};
+
+struct Fp8FwdArgs {
+  const void* q8;  // (B, Hq, Nqp, d) codes
+  const uint8_t* q_scales;
+  const void* k8;  // (B, Hkv, Nkp, d)
+  const uint8_t* k_scales;
+  const void* vt8;  // (B, Hkv, d, Nkp)
+  const uint8_t* v_scales;
+  void* o;     // (B, Nq, Hq, d) bf16
+  float* lse;  // (B, Hq, Nq) or null
+  int B, Hq, Hkv, Nq, Nk, d, causal;
+  float scale;
+};
+
+constexpr int kFp8Block = 64;       // rows per quantisation block
+constexpr int kFp8MaxKeys = 65536;  // keys per sequence the FP8 forward accepts
+int fp8_padded_rows(int n);         // n rounded up to kFp8Block
+bool fp8_quant_supported(int d);
+bool fp8_fwd_supported(int d);
+hipError_t launch_quant_fp8(const Fp8QuantArgs& a, hipStream_t stream);
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream);
+
 // Keys per split for a cache of `capacity` rows cut into `num_splits`
 // pieces: the smallest multiple of the decode key tile >= ceil(cap / S).
 int decode_chunk(int capacity, int num_splits);

@@ -222,6 +222,51 @@ fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const 
                                         int Hkv, int page_size, int pages_per_seq, int num_pages, int d, float scale,
                                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- FP8 (e4m3) forward (FlashAttention: Part 2, section 1.6 "FA3 FP8":
+ * block quantisation plus incoherent processing; the computation is still
+ * exact attention, its arithmetic FP8). Quantise Q, K and V with
+ * fa_quantize_fp8, then run fa_fwd_fp8 on the codes. */
+
+/* Rows of a quantised head: n rounded up to a multiple of 64 (0 for n <= 0). */
+int fa_fp8_padded_rows(int n);
+
+/* Block quantisation of a bf16 tensor x (B, N, H, d) to e4m3 codes, one
+ * scale per 64-row block of each (batch, head). Rows of a block are
+ * optionally rotated first by R = H_d diag(signs) / sqrt(d) (H_d the
+ * Sylvester Hadamard matrix; signs: d device floats, each +1 or -1, or NULL
+ * for no rotation). Rotate Q and K with the same signs and leave V
+ * unrotated: Q K^T, and so the attention, is unchanged.
+ * A block's scale is 2^e with e the smallest integer such that the block's
+ * largest |value| <= 448 * 2^e (e = 0 for an all-zero block, clamped to
+ * [-127, 127]); codes are round-to-nearest-even e4m3 (OCP E4M3: bias 7,
+ * largest finite 448) of value * 2^-e. Outputs, with Np =
+ * fa_fp8_padded_rows(N) and padding rows written as code 0:
+ *   codes  : (B, H, Np, d) bytes, or (B, H, d, Np) when transpose = 1 (the
+ *            layout fa_fwd_fp8 takes for V)
+ *   scales : (B, H, Np / 64) bytes, E8M0: 127 + e
+ * Inputs must be finite. d in {64, 128, 256}; B, H <= 65535.
+ * FA_ERR_INVALID_ARG for negative sizes, transpose not 0/1 or a NULL
+ * buffer; B == 0 or N == 0 is a no-op. */
+fa_status_t fa_quantize_fp8(const void* x, const float* signs, void* codes, uint8_t* scales, int transpose,
+                            int B, int N, int H, int d, void* stream);
+
+/* Attention on FP8 operands: O = softmax(scale * Qh Kh^T) Vh with Qh, Kh, Vh
+ * the dequantised codes (per-block scales applied exactly by the MFMA's
+ * E8M0 scale operands). Both products run on the FP8 MFMA: the
+ * probabilities are quantised as e4m3 of 2^(t - m + 6), t = scale log2(e)
+ * (Qh Kh^T) and m an integer reference >= max t - 2, so every probability
+ * code is that of the row's own maximum up to a power of two; the
+ * denominator sums the unquantised probabilities.
+ *   q8 (B, Hq, Nqp, d), k8 (B, Hkv, Nkp, d), vt8 (B, Hkv, d, Nkp) codes and
+ *   their scales, as fa_quantize_fp8 writes them (Nqp, Nkp = padded Nq, Nk)
+ *   o   : (B, Nq, Hq, d) bfloat16     lse : (B, Hq, Nq) float32 or NULL
+ * causal is top-left (key j visible to query i iff j <= i). A row that sees
+ * no key gets o = 0, lse = -inf. d = 128; Nk <= 65536; Hq % Hkv == 0.
+ * Error codes as fa_fwd. */
+fa_status_t fa_fwd_fp8(const void* q8, const uint8_t* q_scales, const void* k8, const uint8_t* k_scales,
+                       const void* vt8, const uint8_t* v_scales, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale, void* stream);
+
 /* Bytes of device workspace fa_bwd needs: two float32 values (D_i and
  * -LSE_i / scale) per (batch, query head, query), the query count rounded
  * up to a multiple of 32. 0 when B, Hq or Nq is not positive. */

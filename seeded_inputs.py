@@ -19,6 +19,8 @@ __all__ = [
     "prefill_inputs",
     "decode_inputs",
     "poison_cache_tail",
+    "fp8_inputs",
+    "random_signs",
 ]
 
 # Workloads, named by what they are. "std" is the standard deviation of the
@@ -93,3 +95,39 @@ def poison_cache_tail(kcache, vcache, seqlens, k_value=1.0e4, v_value=float("nan
         kcache[b, n:] = k_value
         vcache[b, n:] = v_value
     return kcache, vcache
+
+
+def _codes(shape, std, gen, device):
+    # random e4m3 codes: normal draws (clipped to the format's +-448) cast by
+    # torch to float8_e4m3fn, viewed as bytes
+    x = _normal(shape, std, gen, device).clamp_(-448.0, 448.0)
+    return x.to(torch.float8_e4m3fn).view(torch.uint8)
+
+
+def fp8_inputs(B, Hq, Hkv, Nq, Nk, d, seed=0, device="cpu", code_std=64.0, exp_lo=-7, exp_hi=-6):
+    """Random e4m3 operands in the layout of the FP8 forward: q8 (B, Hq, Nqp,
+    d), k8 (B, Hkv, Nkp, d), vt8 (B, Hkv, d, Nkp) uint8 codes (rows past Nq /
+    Nk are code 0; Nqp, Nkp = lengths rounded up to 64) and per-64-row scale
+    bytes 127 + e, e uniform in [exp_lo, exp_hi] (by default values of
+    standard deviation 0.5 to 1, the scale of the N(0, 1) workloads). Draw
+    order: q, k, v codes, then q, k, v exponents."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    Nqp, Nkp = -(-Nq // 64) * 64, -(-Nk // 64) * 64
+    q8 = torch.zeros((B, Hq, Nqp, d), dtype=torch.uint8, device=device)
+    k8 = torch.zeros((B, Hkv, Nkp, d), dtype=torch.uint8, device=device)
+    vt8 = torch.zeros((B, Hkv, d, Nkp), dtype=torch.uint8, device=device)
+    q8[:, :, :Nq] = _codes((B, Hq, Nq, d), code_std, gen, device)
+    k8[:, :, :Nk] = _codes((B, Hkv, Nk, d), code_std, gen, device)
+    vt8[:, :, :, :Nk] = _codes((B, Hkv, d, Nk), code_std, gen, device)
+    exps = [torch.randint(exp_lo, exp_hi + 1, (B, H, n // 64), generator=gen, device=device, dtype=torch.int32)
+            for H, n in ((Hq, Nqp), (Hkv, Nkp), (Hkv, Nkp))]
+    qs, ks, vs = ((e + 127).to(torch.uint8) for e in exps)
+    return q8, qs, k8, ks, vt8, vs
+
+
+def random_signs(d, seed=0, device="cpu"):
+    """(d,) float32 of independent +-1 (the random diagonal of a rotation)."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(seed))
+    return (torch.randint(0, 2, (d,), generator=gen, device=device, dtype=torch.int32) * 2 - 1).to(torch.float32)

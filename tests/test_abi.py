@@ -178,3 +178,30 @@ def test_append_host_validation():
                                              page, 4, 16, 128, 0.1, null, 0, null)
     assert paged(page=96) == fa.FA_ERR_INVALID_ARG
     assert paged(bt=null) == fa.FA_ERR_INVALID_ARG
+
+
+def test_fp8_host_validation():
+    import ctypes
+    L = fa.lib()
+    null = None
+    fake = ctypes.c_void_p(64)  # never dereferenced: every case fails or ends before a launch
+    assert fa.fa_fp8_padded_rows(1) == 64 and fa.fa_fp8_padded_rows(64) == 64 and fa.fa_fp8_padded_rows(65) == 128
+    assert fa.fa_fp8_padded_rows(0) == 0
+    def quant(x=fake, codes=fake, scales=fake, transpose=0, B=1, N=10, H=2, d=128):
+        return L.fa_quantize_fp8(x, null, codes, scales, transpose, B, N, H, d, null)
+    assert quant(d=96) == fa.FA_ERR_UNSUPPORTED
+    assert quant(transpose=2) == fa.FA_ERR_INVALID_ARG
+    assert quant(x=null) == fa.FA_ERR_INVALID_ARG
+    assert quant(scales=null) == fa.FA_ERR_INVALID_ARG
+    assert quant(N=-1) == fa.FA_ERR_INVALID_ARG
+    assert quant(N=0, x=null) == fa.FA_OK
+    def fwd(q=fake, k=fake, o=fake, B=1, Hq=4, Hkv=2, Nq=100, Nk=100, d=128, causal=0, scale=0.1):
+        return L.fa_fwd_fp8(q, fake, k, fake, fake, fake, o, null, B, Hq, Hkv, Nq, Nk, d, causal, scale, null)
+    assert fwd(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(Hq=3) == fa.FA_ERR_INVALID_ARG
+    assert fwd(causal=2) == fa.FA_ERR_INVALID_ARG
+    assert fwd(scale=float("nan")) == fa.FA_ERR_INVALID_ARG
+    assert fwd(Nk=65537) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(q=null) == fa.FA_ERR_INVALID_ARG
+    assert fwd(k=null) == fa.FA_ERR_INVALID_ARG
+    assert fwd(k=null, Nk=0, q=null, Nq=0) == fa.FA_OK
