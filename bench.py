@@ -274,7 +274,7 @@ def main():
     # block-quantised (outside the attention's clock, timed on its own),
     # then fa_fwd_fp8; its TFLOP/s is priced against the dense FP8 peak.
     fp8 = None
-    if args.fp8_steps > 0 and wp["dtype"] == "bf16" and wp["d"] == 128 and wp["Nk"] <= 65536:
+    if args.fp8_steps > 0 and wp["dtype"] == "bf16" and wp["d"] in (64, 128, 256) and wp["Nk"] <= 65536:
         signs = SI.random_signs(wp["d"], seed=wp["seed"] + 4000).to(dev)
         q8, qs8 = fa.fa_quantize_fp8(q, signs=signs)
         k8, ks8 = fa.fa_quantize_fp8(k, signs=signs)
@@ -309,7 +309,7 @@ def main():
         torch.cuda.synchronize()
         q_ms = sum(e0.elapsed_time(e1) for e0, e1 in qev) / len(qev)
         f_tf = prefill_flops(wp) / (f_ms * 1e-3) / 1e12
-        fp8 = {"value": round(f_tf, 2), "unit": "TFLOP/s", "kernel": "fwd_fp8_kernel<128>", "dtype": "e4m3",
+        fp8 = {"value": round(f_tf, 2), "unit": "TFLOP/s", "kernel": f"fwd_fp8_kernel<{wp['d']}>", "dtype": "e4m3",
                "peak": PEAK_FP8_TFLOPS, "frac": round(f_tf / PEAK_FP8_TFLOPS, 4), "mean_launch_ms": round(f_ms, 5),
                "quantize_ms": round(q_ms, 5), "steps": args.fp8_steps}
         del q8, k8, vt8, o8

@@ -194,14 +194,21 @@ struct F8Cfg {
   static constexpr int TILE = BN * D;            // bytes of a K tile and of a V^T tile
   static constexpr int V_REGION = NST * TILE;    // K tiles, then V^T tiles
   static constexpr int DMA = TILE / (THREADS * 16);
-  static_assert(D == 128, "the LDS swizzles below are laid out for 128-byte key rows");
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
   static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0, "tile does not split over the threads");
   static_assert(NST >= 2 && (NST - 2) * 2 * DMA <= 63, "vmcnt range");
 };
 
-// 16-byte chunk swizzle of a K tile row (128 bytes = 8 chunks): the 16 rows
-// one quarter-wave reads together land in distinct LDS bank groups
-__device__ __forceinline__ int swz_k(int row) { return ((row >> 1) & 3) | (((row >> 5) & 1) << 2); }
+// 16-byte chunk swizzle of a K tile row (D bytes = D / 16 chunks): the 16
+// rows one quarter-wave reads together (keys {0..3, 32..35, 4..7, 36..39}
+// of a 32-key block, plus 8) land in distinct 16-byte bank groups of the
+// 256-byte bank window (2 rows of 128 bytes, 4 of 64, 1 of 256)
+template <int D>
+__device__ __forceinline__ int swz_k(int row) {
+  if constexpr (D == 64) return ((row >> 2) & 1) | (((row >> 5) & 1) << 1);
+  else if constexpr (D == 128) return ((row >> 1) & 3) | (((row >> 5) & 1) << 2);
+  else return (row & 7) | (((row >> 5) & 1) << 3);
+}
 // and of a V^T tile row (64 bytes = 4 chunks)
 __device__ __forceinline__ int swz_v(int dim) { return (dim >> 2) & 3; }
 
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
 #pragma unroll
   for (int j = 0; j < C::DMA; ++j) {
     const int slot = j * C::THREADS + tid;
-    const int row = slot / (D / 16), kc = (slot % (D / 16)) ^ swz_k(row);
+    const int row = slot / (D / 16), kc = (slot % (D / 16)) ^ swz_k<D>(row);
     k_dma[j] = (uint32_t)(row * D + 16 * kc);
     const int dim = slot / 4, vc = (slot % 4) ^ swz_v(dim);
     v_dma[j] = (uint32_t)(dim * p.Nkp + 16 * vc);
@@ -307,7 +314,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
 #pragma unroll
     for (int s = 0; s < D / 64; ++s)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) k_off[nb][s][e] = (uint32_t)(kr * D + 16 * ((4 * s + 2 * g + e) ^ swz_k(kr)));
+      for (int e = 0; e < 2; ++e) k_off[nb][s][e] = (uint32_t)(kr * D + 16 * ((4 * s + 2 * g + e) ^ swz_k<D>(kr)));
   }
   uint32_t v_off[D / 32][2];
 #pragma unroll
@@ -338,17 +345,28 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
   auto s_phase = [&](int t, auto stage) __attribute__((always_inline)) {
     const uint32_t stg = lds0 + (uint32_t)(int)stage * C::TILE;
     const int ksc = sc_k[t];
-    i32x8 kf[2][D / 64];
-#pragma unroll
-    for (int s = 0; s < D / 64; ++s)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) kf[nb][s] = lds_read32(stg + k_off[nb][s][0], stg + k_off[nb][s][1]);
     sc[0] = f32x16{};
     sc[1] = f32x16{};
+    if constexpr (D <= 128) {  // every K operand read ahead of the chain
+      i32x8 kf[2][D / 64];
 #pragma unroll
-    for (int s = 0; s < D / 64; ++s)
+      for (int s = 0; s < D / 64; ++s)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma_fp8(kf[nb][s], qf[s], sc[nb], ksc, qsc);
+        for (int nb = 0; nb < 2; ++nb) kf[nb][s] = lds_read32(stg + k_off[nb][s][0], stg + k_off[nb][s][1]);
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma_fp8(kf[nb][s], qf[s], sc[nb], ksc, qsc);
+    } else {  // d = 256: one slab's operands at a time (registers)
+#pragma unroll
+      for (int s = 0; s < D / 64; ++s) {
+        i32x8 kf[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) kf[nb] = lds_read32(stg + k_off[nb][s][0], stg + k_off[nb][s][1]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma_fp8(kf[nb], qf[s], sc[nb], ksc, qsc);
+      }
+    }
   };
 
   auto softmax_phase = [&](int t, auto mask_tag) __attribute__((always_inline)) {
@@ -412,6 +430,8 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
     for (int dt = 0; dt < D / 32; ++dt) {
       const i32x8 vf = lds_read32(stg + v_off[dt][0], stg + v_off[dt][1]);
       acc[dt] = mfma_fp8(vf, pf, acc[dt], vsc, 127);
+      // d = 256: keep each V operand next to its MFMA (registers)
+      if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
@@ -525,7 +545,7 @@ hipError_t launch_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
 
 int fp8_padded_rows(int n) { return (n + kRows - 1) / kRows * kRows; }
 bool fp8_quant_supported(int d) { return d == 64 || d == 128 || d == 256; }
-bool fp8_fwd_supported(int d) { return d == 128; }
+bool fp8_fwd_supported(int d) { return d == 64 || d == 128 || d == 256; }
 
 hipError_t launch_quant_fp8(const Fp8QuantArgs& a, hipStream_t stream) {
   switch (a.d) {
@@ -537,8 +557,12 @@ hipError_t launch_quant_fp8(const Fp8QuantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
-  if (a.d != 128) return hipErrorInvalidValue;
-  return launch_fp8<F8Cfg<128, 2, 2>>(a, stream);
+  switch (a.d) {
+    case 64: return launch_fp8<F8Cfg<64, 2, 3>>(a, stream);
+    case 128: return launch_fp8<F8Cfg<128, 2, 2>>(a, stream);
+    case 256: return launch_fp8<F8Cfg<256, 2, 1>>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace fa

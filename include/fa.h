@@ -261,7 +261,7 @@ fa_status_t fa_quantize_fp8(const void* x, const float* signs, void* codes, uint
  *   their scales, as fa_quantize_fp8 writes them (Nqp, Nkp = padded Nq, Nk)
  *   o   : (B, Nq, Hq, d) bfloat16     lse : (B, Hq, Nq) float32 or NULL
  * causal is top-left (key j visible to query i iff j <= i). A row that sees
- * no key gets o = 0, lse = -inf. d = 128; Nk <= 65536; Hq % Hkv == 0.
+ * no key gets o = 0, lse = -inf. d in {64, 128, 256}; Nk <= 65536; Hq % Hkv == 0.
  * Error codes as fa_fwd. */
 fa_status_t fa_fwd_fp8(const void* q8, const uint8_t* q_scales, const void* k8, const uint8_t* k_scales,
                        const void* vt8, const uint8_t* v_scales, void* o, float* lse,

@@ -197,7 +197,7 @@ def test_fp8_host_validation():
     assert quant(N=0, x=null) == fa.FA_OK
     def fwd(q=fake, k=fake, o=fake, B=1, Hq=4, Hkv=2, Nq=100, Nk=100, d=128, causal=0, scale=0.1):
         return L.fa_fwd_fp8(q, fake, k, fake, fake, fake, o, null, B, Hq, Hkv, Nq, Nk, d, causal, scale, null)
-    assert fwd(d=64) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(d=96) == fa.FA_ERR_UNSUPPORTED
     assert fwd(Hq=3) == fa.FA_ERR_INVALID_ARG
     assert fwd(causal=2) == fa.FA_ERR_INVALID_ARG
     assert fwd(scale=float("nan")) == fa.FA_ERR_INVALID_ARG

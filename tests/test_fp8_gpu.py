@@ -91,23 +91,27 @@ def test_quantize_rotated(d):
     assert len(bad) <= max(2, gc.size // 10000)
 
 
-# (B, Hq, Hkv, Nq, Nk, causal)
+# (B, Hq, Hkv, Nq, Nk, causal, d)
 FWD_CASES = [
-    (1, 2, 2, 128, 128, False),
-    (1, 2, 2, 128, 128, True),
-    (2, 4, 2, 300, 300, True),      # ragged tiles, GQA
-    (1, 4, 1, 200, 333, False),     # Nq < Nk, MQA
-    (1, 2, 2, 333, 100, True),      # Nq > Nk: rows past the keys see all of them
-    (1, 2, 2, 1, 70, False),        # one query
-    (1, 2, 1, 65, 1, False),        # one key
-    (2, 2, 2, 1000, 1000, True),
+    (1, 2, 2, 128, 128, False, 128),
+    (1, 2, 2, 128, 128, True, 128),
+    (2, 4, 2, 300, 300, True, 128),     # ragged tiles, GQA
+    (1, 4, 1, 200, 333, False, 128),    # Nq < Nk, MQA
+    (1, 2, 2, 333, 100, True, 128),     # Nq > Nk: rows past the keys see all of them
+    (1, 2, 2, 1, 70, False, 128),       # one query
+    (1, 2, 1, 65, 1, False, 128),       # one key
+    (2, 2, 2, 1000, 1000, True, 128),
+    (2, 4, 2, 300, 300, True, 64),
+    (1, 2, 1, 200, 333, False, 64),
+    (2, 2, 2, 300, 300, True, 256),
+    (1, 2, 1, 130, 257, False, 256),
 ]
 
 
-@pytest.mark.parametrize("case", FWD_CASES, ids=lambda c: "B{}H{}kv{}q{}k{}{}".format(*c[:5], "c" if c[5] else ""))
+@pytest.mark.parametrize("case", FWD_CASES,
+                         ids=lambda c: "B{}H{}kv{}q{}k{}{}d{}".format(*c[:5], "c" if c[5] else "", c[6]))
 def test_fwd_fp8_matches_oracle(case):
-    B, Hq, Hkv, Nq, Nk, causal = case
-    d = 128
+    B, Hq, Hkv, Nq, Nk, causal, d = case
     note(f"fp8 fwd B={B} Hq={Hq} Hkv={Hkv} Nq={Nq} Nk={Nk} causal={causal}")
     dev = torch.device("cuda")
     ins = SI.fp8_inputs(B, Hq, Hkv, Nq, Nk, d, seed=320 + Nq)
@@ -123,8 +127,13 @@ def test_fwd_fp8_matches_oracle(case):
     fin = np.isfinite(l_ref)
     assert np.array_equal(np.isfinite(L), fin)
     el = float(np.max(np.abs(L[fin] - l_ref[fin]), initial=0.0))
-    note(f"  max|dO|={eo:.3e} (max|O|={np.max(np.abs(o_ref)):.2f}) max|dLSE|={el:.3e}")
-    assert eo <= TOL_O and el <= TOL_LSE
+    # The bf16 bar scaled by the output's size (as the backward tests do): a
+    # probability within float32 rounding of an e4m3 midpoint may take the
+    # other code (kernel scores are float32, the oracle's float64), moving a
+    # row that averages few values by a few percent of one value.
+    tol = TOL_O * max(1.0, float(np.max(np.abs(o_ref))))
+    note(f"  max|dO|={eo:.3e} (max|O|={np.max(np.abs(o_ref)):.2f}, bound {tol:.3e}) max|dLSE|={el:.3e}")
+    assert eo <= tol and el <= TOL_LSE
 
 
 def test_fwd_fp8_no_keys():
@@ -144,21 +153,22 @@ def _pipeline(q, k, v, causal, signs):
                         scale=float(np.float32(1.0 / math.sqrt(q.shape[3]))))
 
 
-def test_fp8_pipeline_error_against_exact_attention():
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_fp8_pipeline_error_against_exact_attention(d):
     # bf16 inputs -> FP8 quantisation -> FP8 attention, against exact fp64
     # attention on the bf16 inputs: the relative RMS error stays at the
     # level e4m3 rounding of Q, K and V allows (about 5% here: early causal
     # rows average few values, each off by up to 2^-4 relative), with and
     # without rotation
     dev = torch.device("cuda")
-    q, k, v = SI.prefill_inputs(B=1, Hq=4, Hkv=2, Nq=512, Nk=512, d=128, seed=340, device=dev)
-    ref, _ = O.attention(f64(q), f64(k), f64(v), True, float(np.float32(1.0 / math.sqrt(128))))
+    q, k, v = SI.prefill_inputs(B=1, Hq=4, Hkv=2, Nq=512, Nk=512, d=d, seed=340, device=dev)
+    ref, _ = O.attention(f64(q), f64(k), f64(v), True, float(np.float32(1.0 / math.sqrt(d))))
     for rot in (False, True):
-        signs = SI.random_signs(128, seed=341).to(dev) if rot else None
+        signs = SI.random_signs(d, seed=341).to(dev) if rot else None
         o, _ = _pipeline(q, k, v, True, signs)
         torch.cuda.synchronize()
         rel = float(np.sqrt(np.mean((f64(o) - ref) ** 2) / np.mean(ref ** 2)))
-        note(f"  rotation={rot}: relative RMS error {rel:.4f}")
+        note(f"  d={d} rotation={rot}: relative RMS error {rel:.4f}")
         assert rel < 0.08
 
 
