@@ -57,6 +57,8 @@ __all__ = [
     "attention_window",
     "attention_varlen",
     "decode_append",
+    "attention_backward_window",
+    "attention_backward_varlen",
 ]
 
 
@@ -443,3 +445,53 @@ def decode_append(q, kcache, vcache, seqlens, k_new, v_new, causal, scale):
             O[b, :, hq] = P @ vc[b, :avail, kv]
             L[b, hq] = lse
     return kc, vc, O, L
+
+
+def attention_backward_window(q, k, v, do, window_left, window_right, scale):
+    """Gradients of ``attention_window``: dq (B, Nq, Hq, d), dk and dv
+    (B, Nk, Hkv, d) in float64.
+
+    The chain rule of ``attention_backward_rows`` applied under the
+    bottom-right aligned window of ``window_mask`` (pyshine.com code tour:
+    bottom-right causal since 2.1, sliding windows since 2.3). A query that
+    sees no key has P = 0 in its row, so it contributes no gradient.
+    """
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    B, Nq, Hq, _ = q.shape
+    Nk, Hkv = k.shape[1], k.shape[2]
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    mask = window_mask(Nq, Nk, window_left, window_right)
+    for b in range(B):
+        for hq in range(Hq):
+            kv = kv_head_of(hq, Hq, Hkv)
+            Q, K, V = _f64(q[b, :, hq]), _f64(k[b, :, kv]), _f64(v[b, :, kv])
+            dO = _f64(do[b, :, hq])
+            P, _ = softmax_rows(scores(Q, K, scale), mask)
+            dP = dO @ V.T
+            dS = P * (dP - np.sum(P * dP, axis=1, keepdims=True))
+            dq[b, :, hq] = float(scale) * (dS @ K)
+            dk[b, :, kv] += float(scale) * (dS.T @ Q)
+            dv[b, :, kv] += P.T @ dO
+    return dq, dk, dv
+
+
+def attention_backward_varlen(q, k, v, do, cu_q, cu_k, window_left, window_right, scale):
+    """Gradients of ``attention_varlen`` for packed q, do (total_q, Hq, d)
+    and k, v (total_k, Hkv, d): each sequence's block is
+    ``attention_backward_window`` of its own rows."""
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    dq = np.zeros(q.shape, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    for b in range(len(cu_q) - 1):
+        qa, qb, ka, kb = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        if qb == qa or kb == ka:
+            continue
+        gq, gk, gv = attention_backward_window(q[None, qa:qb], k[None, ka:kb], v[None, ka:kb], do[None, qa:qb],
+                                               window_left, window_right, scale)
+        dq[qa:qb] = gq[0]
+        dk[ka:kb] = gk[0]
+        dv[ka:kb] = gv[0]
+    return dq, dk, dv

@@ -670,6 +670,75 @@ def pin_attention_fp8_brute_force(tol=1e-12):
                 assert abs(l[0, h, i] - math.log(2.0) * (M + math.log2(den))) <= tol, ("fp8 brute LSE", causal)
 
 
+# ---------------------------------------------------------------------------
+# backward under windows and packed variable-length batches
+# ---------------------------------------------------------------------------
+def _torch_masked_grads(q, k, v, do, mask, scale):
+    """PyTorch float64 autograd of softmax(scale Q K^T + mask) V for one
+    head; rows without a visible key are zeroed before the product."""
+    import torch
+    Q, K, V = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    S = scale * Q @ K.T
+    S = S.masked_fill(~torch.tensor(mask), float("-inf"))
+    P = torch.softmax(S, dim=1)
+    P = torch.where(torch.isnan(P), torch.zeros_like(P), P)
+    O = P @ V
+    O.backward(torch.tensor(do, dtype=torch.float64))
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy()
+
+
+def pin_backward_window_torch_autograd(tol=1e-10):
+    """Bottom-right windows (causal and sliding, Nq != Nk, rows with no key)
+    against PyTorch float64 autograd with an explicit mask (built here by
+    plain loops)."""
+    r = np.random.default_rng(2500)
+    B, Hq, Hkv, d = 1, 4, 2, 5
+    for Nq, Nk, wl, wr in ((6, 9, -1, 0), (9, 6, -1, 0), (8, 8, 2, 1), (7, 10, 3, -1), (5, 5, 0, 0)):
+        q = r.normal(size=(B, Nq, Hq, d))
+        k = r.normal(size=(B, Nk, Hkv, d))
+        v = r.normal(size=(B, Nk, Hkv, d))
+        do = r.normal(size=(B, Nq, Hq, d))
+        gq, gk, gv = O.attention_backward_window(q, k, v, do, wl, wr, 0.6)
+        off = Nk - Nq
+        mask = np.array([[(wl < 0 or j >= i + off - wl) and (wr < 0 or j <= i + off + wr) for j in range(Nk)]
+                         for i in range(Nq)])
+        rk = np.zeros_like(gk)
+        rv = np.zeros_like(gv)
+        for h in range(Hq):
+            kv = (h * Hkv) // Hq
+            tq, tk, tv = _torch_masked_grads(q[0, :, h], k[0, :, kv], v[0, :, kv], do[0, :, h], mask, 0.6)
+            assert np.max(np.abs(gq[0, :, h] - tq)) <= tol, ("window dq", Nq, Nk, wl, wr)
+            rk[0, :, kv] += tk
+            rv[0, :, kv] += tv
+        assert np.max(np.abs(gk - rk)) <= tol and np.max(np.abs(gv - rv)) <= tol, ("window dk/dv", Nq, Nk, wl, wr)
+
+
+def pin_backward_varlen_concatenation(tol=1e-12):
+    """A packed batch's gradients are its sequences' own, laid end to end
+    (sequences pinned one by one against autograd above)."""
+    r = np.random.default_rng(2510)
+    lq, lk = [3, 0, 5, 2], [4, 2, 5, 6]
+    cu_q, cu_k = np.concatenate([[0], np.cumsum(lq)]), np.concatenate([[0], np.cumsum(lk)])
+    q = r.normal(size=(cu_q[-1], 2, 3))
+    k = r.normal(size=(cu_k[-1], 1, 3))
+    v = r.normal(size=(cu_k[-1], 1, 3))
+    do = r.normal(size=(cu_q[-1], 2, 3))
+    for wl, wr in ((-1, -1), (-1, 0), (1, 1)):
+        gq, gk, gv = O.attention_backward_varlen(q, k, v, do, cu_q, cu_k, wl, wr, 0.7)
+        for b in range(4):
+            qs, ks = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+            if lq[b] == 0:
+                assert not gk[ks].any() and not gv[ks].any(), "keys of a sequence without queries"
+                continue
+            mask = np.array([[(wl < 0 or j >= i + lk[b] - lq[b] - wl) and (wr < 0 or j <= i + lk[b] - lq[b] + wr)
+                              for j in range(lk[b])] for i in range(lq[b])])
+            tq, tk, tv = _torch_masked_grads(q[qs, :, :].transpose(1, 0, 2)[0], k[ks, 0], v[ks, 0],
+                                             do[qs].transpose(1, 0, 2)[0], mask, 0.7)
+            tq1, tk1, tv1 = _torch_masked_grads(q[qs, 1], k[ks, 0], v[ks, 0], do[qs, 1], mask, 0.7)
+            assert np.max(np.abs(gq[qs, 0] - tq)) <= 1e-10 and np.max(np.abs(gq[qs, 1] - tq1)) <= 1e-10
+            assert np.max(np.abs(gk[ks, 0] - (tk + tk1))) <= 1e-10 and np.max(np.abs(gv[ks, 0] - (tv + tv1))) <= 1e-10
+
+
 ALL_PINS = [
     pin_brute_force,
     pin_torch_sdpa,
@@ -706,4 +775,6 @@ ALL_PINS = [
     pin_attention_fp8_exact_probabilities,
     pin_attention_fp8_error_bound,
     pin_attention_fp8_brute_force,
+    pin_backward_window_torch_autograd,
+    pin_backward_varlen_concatenation,
 ]

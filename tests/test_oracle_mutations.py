@@ -15,7 +15,8 @@ from oracle import sdpa as O
 _orig = {n: getattr(O, n) for n in ("kv_head_of", "visible_mask", "scores", "softmax_rows",
                                     "attention_rows", "decode", "merge_partials",
                                     "online_softmax_attention", "attention_backward_rows", "decode_paged",
-                                    "window_mask", "attention_varlen", "decode_append")}
+                                    "window_mask", "attention_varlen", "decode_append",
+                                    "attention_backward_window", "attention_backward_varlen")}
 
 
 def _interleaved_groups(hq, Hq, Hkv):
@@ -208,6 +209,23 @@ def _append_variant(kind):
     return f
 
 
+def _bwd_window_top_left(q, k, v, do, window_left, window_right, scale):
+    # windows aligned to the top-left corner: pretend Nk = Nq for the offset
+    saved = O.window_mask
+    O.window_mask = lambda Nq, Nk, wl, wr, rows=None: _window_top_left(Nq, Nk, wl, wr, rows)
+    try:
+        return _orig["attention_backward_window"](q, k, v, do, window_left, window_right, scale)
+    finally:
+        O.window_mask = saved
+
+
+def _bwd_varlen_keys_of_next(q, k, v, do, cu_q, cu_k, window_left, window_right, scale):
+    # off by one sequence in the key offsets
+    cu_k2 = np.concatenate([cu_k[1:], [cu_k[-1]]]) if len(cu_k) > 2 else cu_k
+    cu_k2 = np.maximum.accumulate(np.concatenate([[0], cu_k2[1:]]))
+    return _orig["attention_backward_varlen"](q, k, v, do, cu_q, cu_k2, window_left, window_right, scale)
+
+
 MUTATIONS = [
     ("kv_head_of", _interleaved_groups),
     ("visible_mask", _strict_causal),
@@ -234,6 +252,8 @@ MUTATIONS = [
     ("decode_append", _append_variant("shifted_write")),
     ("decode_append", _append_variant("old_length")),
     ("decode_append", _append_variant("top_left")),
+    ("attention_backward_window", _bwd_window_top_left),
+    ("attention_backward_varlen", _bwd_varlen_keys_of_next),
 ]
 
 
