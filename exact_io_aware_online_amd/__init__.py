@@ -29,6 +29,8 @@ __all__ = [
     "fa_quantize_fp8",
     "fa_fwd_fp8",
     "fa_bwd",
+    "fa_bwd_window",
+    "fa_bwd_varlen",
     "fa_bwd_workspace_size",
     "FA_DTYPE_BF16",
     "FA_DTYPE_F32",
@@ -91,6 +93,11 @@ def lib():
     L.fa_bwd_workspace_size.argtypes = [i, i, i]
     L.fa_bwd.restype = i
     L.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_bwd_window.restype = i
+    L.fa_bwd_window.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_bwd_varlen.restype = i
+    L.fa_bwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, i, f, vp, sz,
+                                vp]
     _lib = L
     return L
 
@@ -544,4 +551,63 @@ def fa_bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv
                       _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def fa_bwd_window(q, k, v, o, lse, dout, window_left, window_right, scale=None, dq=None, dk=None, dv=None,
+                  workspace=None, stream=None):
+    """Attention backward under a bottom-right aligned window through
+    ``fa_bwd_window``; shapes as ``fa_bwd``. Returns (dq, dk, dv)."""
+    import torch
+    B, Nq, Hq, d = q.shape
+    _, Nk, Hkv, _ = k.shape
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(lse, "lse", torch.float32, q.device)
+    need = fa_bwd_workspace_size(B, Hq, Nq)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), B, Hq, Hkv, Nq, Nk, d, int(window_left), int(window_right), float(scale),
+                             _ptr(workspace), ws_bytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_window")
+    return dq, dk, dv
+
+
+def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, window_left=-1,
+                  window_right=-1, scale=None, dq=None, dk=None, dv=None, workspace=None, stream=None):
+    """Attention backward over a packed batch through ``fa_bwd_varlen``:
+    q, o, dout (total_q, Hq, d), k, v (total_k, Hkv, d) bf16, lse (Hq,
+    total_q) float32 as ``fa_fwd_varlen`` returns it. Returns (dq, dk, dv)."""
+    import torch
+    total_q, Hq, d = q.shape
+    total_k, Hkv, _ = k.shape
+    B = cu_seqlens_q.shape[0] - 1
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(lse, "lse", torch.float32, q.device)
+    _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
+    _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
+    need = fa_bwd_workspace_size(B, Hq, max_seqlen_q)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                             _ptr(dv), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), B, Hq, Hkv, int(max_seqlen_q),
+                             int(max_seqlen_k), total_q, total_k, d, int(window_left), int(window_right),
+                             float(scale), _ptr(workspace), ws_bytes, _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_bwd_varlen")
     return dq, dk, dv

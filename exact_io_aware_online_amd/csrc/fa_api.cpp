@@ -333,13 +333,19 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq) {
   return fa::bwd_workspace_bytes(B, Hq, Nq);
 }
 
-fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                   const void* dout, void* dq, void* dk, void* dv,
-                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
-                   void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0) return FA_ERR_INVALID_ARG;
+namespace {
+
+// Shared checks and dispatch of the three backward entry points. Nq and Nk
+// are the (longest) sequence lengths; for a packed batch total_q / total_k
+// are the packed row counts and cu_q / cu_k the sequence offsets.
+fa_status_t bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                void* dq, void* dk, void* dv, const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv,
+                int Nq, int Nk, int total_q, int total_k, int d, int window_left, int window_right,
+                int bottom_right, float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const bool packed = cu_q != nullptr || cu_k != nullptr;
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Nq < 0 || Nk < 0 || d <= 0 || total_q < 0 || total_k < 0)
+    return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
-  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED;
   // one-dimensional grids, and the workspace addressed with 32-bit offsets
@@ -347,10 +353,13 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   if ((((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff || (((int64_t)Nk + 127) / 128) * Hkv * B > 0x7fffffff ||
       2 * (int64_t)B * Hq * nq_pad * 4 > 0xffffffffLL || Hq > 65535 || B > 65535)
     return FA_ERR_UNSUPPORTED;
-  if (B == 0 || (Nq == 0 && Nk == 0)) return FA_OK;
-  if (Nq > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
+  const int64_t rows_q = packed ? total_q : (int64_t)B * Nq;
+  const int64_t rows_k = packed ? total_k : (int64_t)B * Nk;
+  if (B == 0 || (rows_q == 0 && rows_k == 0)) return FA_OK;
+  if (packed && (cu_q == nullptr || cu_k == nullptr)) return FA_ERR_INVALID_ARG;
+  if (rows_q > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))
     return FA_ERR_INVALID_ARG;
-  if (Nk > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return FA_ERR_INVALID_ARG;
+  if (rows_k > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr)) return FA_ERR_INVALID_ARG;
   const size_t need = Nq > 0 ? fa::bwd_workspace_bytes(B, Hq, Nq) : 0;
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
 
@@ -370,10 +379,46 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
   a.Nq = Nq;
   a.Nk = Nk;
   a.d = d;
-  a.causal = causal;
   a.scale = scale;
   a.workspace = workspace;
+  a.window_left = window_left < 0 ? -1 : window_left;
+  a.window_right = window_right < 0 ? -1 : window_right;
+  a.bottom_right = bottom_right;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.total_q = total_q;
+  a.total_k = total_k;
   return launch_status(fa::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
+                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (causal != 0 && causal != 1) return FA_ERR_INVALID_ARG;
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, 0, 0, d, -1, causal ? 0 : -1, 0,
+             scale, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int window_left, int window_right,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, nullptr, nullptr, B, Hq, Hkv, Nq, Nk, 0, 0, d, window_left,
+             window_right, 1, scale, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                          int d, int window_left, int window_right, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return FA_ERR_INVALID_ARG;
+  return bwd(q, k, v, o, lse, dout, dq, dk, dv, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, max_seqlen_q, max_seqlen_k,
+             total_q, total_k, d, window_left, window_right, 1, scale, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

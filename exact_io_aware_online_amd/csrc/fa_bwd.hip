@@ -42,13 +42,47 @@ struct BwdParams {
   char* __restrict__ dq;
   char* __restrict__ dk;
   char* __restrict__ dv;
-  float* __restrict__ dvec;  // D, (B, Hq, nq_pad)
+  float* __restrict__ dvec;  // D, (B, Hq, nq_pad), rows local to their sequence
   float* __restrict__ nlse;  // -LSE / scale, (B, Hq, nq_pad)
-  int Nq, Nk, Hq, Hkv, group, B, causal;
+  int Nq, Nk, Hq, Hkv, group, B;  // dense lengths (packed batches: the longest sequences)
   int nq_pad;                // Nq rounded up to a multiple of kQStep
   float c;                   // scale * log2(e)
   float scale;
+  // key j is visible to query i iff i + off - wl <= j <= i + off + wr (a
+  // negative bound is unlimited), off = Nk_b - Nq_b when bottom_right,
+  // else 0; top-left causal is (wl, wr) = (-1, 0)
+  int wl, wr, bottom_right;
+  int lpt;                   // dQ tiles longest-first (later query tiles see more keys)
+  // packed variable-length batch (null: dense): sequence b is rows
+  // cu_q[b] .. cu_q[b+1] of q, o, dout, dq and cu_k[b] .. cu_k[b+1] of k, v, dk, dv
+  const int32_t* __restrict__ cu_q;
+  const int32_t* __restrict__ cu_k;
+  int total_q, total_k;      // packed row counts (LSE is then (Hq, total_q))
 };
+
+// One sequence's rows: where its queries and keys start in the (packed or
+// dense) arrays, how many there are, and the window offset.
+struct Seq {
+  int qrow0, Nqb, krow0, Nkb, off;
+};
+
+template <bool WIN>
+__device__ __forceinline__ Seq seq_of(const BwdParams& p, int b) {
+  Seq s;
+  if (WIN && p.cu_q != nullptr) {  // offsets clamped into the arrays
+    s.qrow0 = min(max(p.cu_q[b], 0), p.total_q);
+    s.Nqb = min(min(max(p.cu_q[b + 1], s.qrow0), p.total_q) - s.qrow0, p.Nq);
+    s.krow0 = min(max(p.cu_k[b], 0), p.total_k);
+    s.Nkb = min(min(max(p.cu_k[b + 1], s.krow0), p.total_k) - s.krow0, p.Nk);
+  } else {
+    s.qrow0 = b * p.Nq;
+    s.Nqb = p.Nq;
+    s.krow0 = b * p.Nk;
+    s.Nkb = p.Nk;
+  }
+  s.off = WIN && p.bottom_right ? s.Nkb - s.Nqb : 0;
+  return s;
+}
 
 // queries per step of the dK/dV kernel (and the padding unit); 64 was
 // measured to spill the single-pass kernel's 512 registers per lane
@@ -67,13 +101,15 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   const int64_t total = (int64_t)p.B * p.Hq * p.nq_pad;
   float acc = 0.f;
   int i = 0, h = 0, b = 0;
+  Seq sq{0, 0, 0, 0, 0};
   if (row < total) {
     i = (int)(row % p.nq_pad);
     const int64_t bh = row / p.nq_pad;
     h = (int)(bh % p.Hq);
     b = (int)(bh / p.Hq);
-    if (i < p.Nq) {
-      const int64_t off = (((int64_t)b * p.Nq + i) * p.Hq + h) * D * 2 + part * 16;
+    sq = seq_of<true>(p, b);
+    if (i < sq.Nqb) {
+      const int64_t off = (((int64_t)sq.qrow0 + i) * p.Hq + h) * D * 2 + part * 16;
       const bf16x8 x = *reinterpret_cast<const bf16x8*>(p.dout + off);
       const bf16x8 y = *reinterpret_cast<const bf16x8*>(p.o + off);
 #pragma unroll
@@ -84,8 +120,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   for (int w = TPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w, 64);
   if (row < total && part == 0) {
     float nl = -INFINITY;  // padded rows: P = 0
-    if (i < p.Nq) {
-      const float l = p.lse[((int64_t)b * p.Hq + h) * p.Nq + i];
+    if (i < sq.Nqb) {
+      const int64_t li = p.cu_q != nullptr ? (int64_t)h * p.total_q + sq.qrow0 + i : ((int64_t)b * p.Hq + h) * p.Nq + i;
+      const float l = p.lse[li];
       nl = l == -INFINITY ? -INFINITY : -l / p.scale;
     }
     p.dvec[row] = acc;
@@ -106,7 +143,10 @@ struct DqCfg {
   static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0 && BN % 32 == 0, "dq tile");
 };
 
-template <class C>
+// WIN: general windows and packed batches; otherwise dense, with at most a
+// top-left causal mask (window (-1, 0) or (-1, -1)), compiled without the
+// general bounds
+template <class C, bool WIN>
 __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int n_qtiles) {
   constexpr int D = C::D, BN = C::BN, NST = C::NST, CPR = C::CPR, NBT = BN / 32;
   __shared__ __attribute__((aligned(1024))) char smem[2 * NST * C::TILE];
@@ -128,18 +168,23 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
   const int b = pr / p.Hkv;
   const int kvh = pr - b * p.Hkv;
   const int hq = kvh * p.group + j;
-  const int qt = p.causal ? n_qtiles - 1 - r : r;
+  const int qt = p.lpt ? n_qtiles - 1 - r : r;
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
+  const Seq sq = seq_of<WIN>(p, b);
+  if (q0 >= sq.Nqb) return;  // whole workgroup: past this sequence's queries
 
   const int64_t q_row = (int64_t)p.Hq * D * 2;
   const int kv_row = p.Hkv * D * 2;
-  int kend = p.Nk;
-  if (p.causal) kend = min(kend, q0 + C::BM);
-  const int ntiles = kend > 0 ? (kend + BN - 1) / BN : 0;
+  // keys some row of the tile sees: tiles t0 .. t0 + ntiles - 1
+  const int q_last = min(q0 + C::BM, sq.Nqb) - 1;
+  const int klo = p.wl >= 0 ? max(q0 + sq.off - p.wl, 0) : 0;
+  const int khi = p.wr >= 0 ? min(q_last + sq.off + p.wr, sq.Nkb - 1) : sq.Nkb - 1;
+  const int t0 = klo / BN;
+  const int ntiles = khi >= klo ? khi / BN - t0 + 1 : 0;
 
-  const char* kbase = p.k + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
-  const char* vbase = p.v + ((int64_t)b * p.Nk * p.Hkv + kvh) * D * 2;
+  const char* kbase = p.k + ((int64_t)sq.krow0 * p.Hkv + kvh) * D * 2;
+  const char* vbase = p.v + ((int64_t)sq.krow0 * p.Hkv + kvh) * D * 2;
   int dma_row[C::DMA], dma_col[C::DMA];
 #pragma unroll
   for (int jj = 0; jj < C::DMA; ++jj) {
@@ -149,11 +194,11 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
   }
   const uint32_t dma_lds = __builtin_amdgcn_readfirstlane(lds0 + wave * 64 * 16);
   auto issue_tile = [&](int t) __attribute__((always_inline)) {
-    const int j0 = t * BN;
+    const int j0 = (t0 + t) * BN;
     const char* ks = kbase + (int64_t)j0 * kv_row;
     const char* vs = vbase + (int64_t)j0 * kv_row;
     const uint32_t st = dma_lds + (uint32_t)((t % NST) * C::TILE);
-    const int last = p.Nk - 1 - j0;  // rows past the end re-read the last key (masked later)
+    const int last = sq.Nkb - 1 - j0;  // rows past the end re-read the last key (masked later)
 #pragma unroll
     for (int jj = 0; jj < C::DMA; ++jj) {
       const uint32_t off = (uint32_t)(min(dma_row[jj], last) * kv_row + dma_col[jj]);
@@ -167,11 +212,11 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
   const int my_q = qw0 + r32;
   bf16x8 qf[D / 16], of[D / 16];
   {
-    const int64_t off = ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
+    const int64_t off = ((int64_t)sq.qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      qf[ks] = my_q < p.Nq ? *reinterpret_cast<const bf16x8*>(p.q + off + (ks * 16 + g * 8) * 2) : bf16x8{};
-      of[ks] = my_q < p.Nq ? *reinterpret_cast<const bf16x8*>(p.dout + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      qf[ks] = my_q < sq.Nqb ? *reinterpret_cast<const bf16x8*>(p.q + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      of[ks] = my_q < sq.Nqb ? *reinterpret_cast<const bf16x8*>(p.dout + off + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
   const int64_t vec = ((int64_t)b * p.Hq + hq) * p.nq_pad + min(my_q, p.nq_pad - 1);
@@ -205,12 +250,22 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = f32x16{};
 
-  int nt_w = ntiles, nt_full = p.Nk / BN;
-  if (p.causal) {
-    nt_w = min(ntiles, (qw0 + 31) / BN + 1);
-    nt_full = min(nt_full, (qw0 + 1) / BN);
+  // This wavefront's tiles (relative to t0): [t_lo, t_hi) hold a key some
+  // of its rows see, [u_lo, u_hi) only keys all of its rows see (no mask).
+  int t_lo = 0, t_hi = 0, u_lo = 0, u_hi = 0;
+  {
+    const int wq_last = min(qw0 + 31, sq.Nqb - 1);
+    const int wlo = p.wl >= 0 ? max(qw0 + sq.off - p.wl, 0) : 0;
+    const int whi = p.wr >= 0 ? min(wq_last + sq.off + p.wr, sq.Nkb - 1) : sq.Nkb - 1;
+    if (wq_last >= qw0 && whi >= wlo) {
+      t_lo = max(wlo / BN - t0, 0);
+      t_hi = min(whi / BN - t0 + 1, ntiles);
+      const int flo = p.wl >= 0 ? max(wq_last + sq.off - p.wl, 0) : 0;
+      const int fhi = p.wr >= 0 ? min(qw0 + sq.off + p.wr, sq.Nkb - 1) : sq.Nkb - 1;
+      u_lo = min(max((flo + BN - 1) / BN - t0, t_lo), t_hi);
+      u_hi = min(max((fhi + 1) / BN - t0, u_lo), t_hi);
+    }
   }
-  nt_full = min(nt_full, nt_w);
 
   auto compute_tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
@@ -228,9 +283,12 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
         s[nb] = mfma32x32x16(ka, qf[ks], s[nb]);
         dp[nb] = mfma32x32x16(va, of[ks], dp[nb]);
       }
-    // dS^T = P^T o (dP^T - D), P^T = 2^(c s - c LSE / scale)
+    // dS^T = P^T o (dP^T - D), P^T = 2^(c s - c LSE / scale); key
+    // j0 + 4 g + o (o = 32 nb + 8 (i/4) + i%4) is visible iff lo <= o <= hi
     bf16x8 dsf[BN / 16];
-    const int lim = (p.causal ? min(p.Nk - 1, my_q) : p.Nk - 1) - t * BN - 4 * g;
+    const int jb = (t0 + t) * BN + 4 * g;
+    const int lo = (p.wl >= 0 ? my_q + sq.off - p.wl : 0) - jb;
+    const int hi = (p.wr >= 0 ? min(my_q + sq.off + p.wr, sq.Nkb - 1) : sq.Nkb - 1) - jb;
 #pragma unroll
     for (int kk = 0; kk < BN / 16; ++kk) {
       const int nb = kk >> 1, h = (kk & 1) * 8;
@@ -240,7 +298,11 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
         float pv = exp2_fast(fmaf(s[nb][h + i], p.c, cnl));
         if constexpr (MASK) {
           const int off = nb * 32 + 8 * ((h + i) >> 2) + ((h + i) & 3);
-          if (off > lim) pv = 0.f;
+          if constexpr (WIN) {
+            if (off < lo || off > hi) pv = 0.f;
+          } else {
+            if (off > hi) pv = 0.f;
+          }
         }
         e[i] = pv * (dp[nb][h + i] - dval);
       }
@@ -267,18 +329,26 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
     if (t + 1 < ntiles) issue_tile(t + 1);
   };
   int t = 0;
-  for (; t < nt_full; ++t) {
+  if constexpr (WIN) {
+    for (; t < t_lo; ++t) sync_tile(t);
+    for (; t < u_lo; ++t) {
+      sync_tile(t);
+      compute_tile(t, std::true_type{});
+    }
+  }
+  // (dense: t_lo = u_lo = 0)
+  for (; t < u_hi; ++t) {
     sync_tile(t);
     compute_tile(t, std::false_type{});
   }
-  for (; t < nt_w; ++t) {
+  for (; t < t_hi; ++t) {
     sync_tile(t);
     compute_tile(t, std::true_type{});
   }
   for (; t < ntiles; ++t) sync_tile(t);
 
-  if (my_q < p.Nq) {
-    char* row = p.dq + ((int64_t)b * p.Nq + my_q) * q_row + (int64_t)hq * D * 2;
+  if (my_q < sq.Nqb) {
+    char* row = p.dq + ((int64_t)sq.qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -313,7 +383,7 @@ struct DkvCfg {
 // wavefronts per SIMD, the pair measured slower than the single pass).
 constexpr int kDV = 1, kDK = 2, kDKDV = 3;
 
-template <class C, int WHAT, int WPS>
+template <class C, int WHAT, int WPS, bool WIN>
 __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, int n_ktiles) {
   constexpr bool DV = (WHAT & kDV) != 0, DK = (WHAT & kDK) != 0;
   constexpr int D = C::D, NST = C::NST, CPR = C::CPR, BQ = C::BQ;
@@ -336,6 +406,7 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   const int k0 = kt * C::BK;
   const int kw0 = k0 + wave * 32;     // first key of this wavefront
   const int my_k = kw0 + r32;         // this lane's key (MFMA column)
+  const Seq sq = seq_of<WIN>(p, b);
 
   const int kv_row = p.Hkv * D * 2;
   const int64_t q_row = (int64_t)p.Hq * D * 2;
@@ -344,21 +415,35 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   // = X[key][16 ks + 8 g + i]
   bf16x8 kf[D / 16], vf[D / 16];
   {
-    const int64_t off = ((int64_t)b * p.Nk + my_k) * kv_row + (int64_t)kvh * D * 2;
+    const int64_t off = ((int64_t)sq.krow0 + my_k) * kv_row + (int64_t)kvh * D * 2;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      kf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.k + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+      kf[ks] = my_k < sq.Nkb ? *reinterpret_cast<const bf16x8*>(p.k + off + (ks * 16 + g * 8) * 2) : bf16x8{};
       if constexpr (DK)
-        vf[ks] = my_k < p.Nk ? *reinterpret_cast<const bf16x8*>(p.v + off + (ks * 16 + g * 8) * 2) : bf16x8{};
+        vf[ks] = my_k < sq.Nkb ? *reinterpret_cast<const bf16x8*>(p.v + off + (ks * 16 + g * 8) * 2) : bf16x8{};
     }
   }
 
-  // steps: query tiles of BQ rows of each query head of the group; with a
-  // causal mask queries below this workgroup's first key see none of it
-  const int q_first = p.causal ? k0 / BQ : 0;
-  const int nqt = (p.Nq + BQ - 1) / BQ;
-  const int per_head = max(nqt - q_first, 0);
-  const int nsteps = k0 < p.Nk ? per_head * p.group : 0;
+  // steps: query tiles of BQ rows of each query head of the group, those
+  // some query of which sees a key of this workgroup: key j is seen by
+  // queries j - off - wr .. j - off + wl
+  int q_first = 0, per_head = 0, nsteps = 0;
+  if constexpr (WIN) {
+    if (k0 < sq.Nkb && sq.Nqb > 0) {
+      const int k_last = min(k0 + C::BK, sq.Nkb) - 1;
+      const int qlo = p.wr >= 0 ? max(k0 - sq.off - p.wr, 0) : 0;
+      const int qhi = p.wl >= 0 ? min(k_last - sq.off + p.wl, sq.Nqb - 1) : sq.Nqb - 1;
+      if (qhi >= qlo) {
+        q_first = qlo / BQ;
+        per_head = qhi / BQ - q_first + 1;
+      }
+    }
+    nsteps = per_head * p.group;
+  } else {  // top-left causal: queries below this workgroup's first key see none of it
+    q_first = p.wr >= 0 ? k0 / BQ : 0;
+    per_head = max((p.Nq + BQ - 1) / BQ - q_first, 0);
+    nsteps = k0 < p.Nk ? per_head * p.group : 0;
+  }
 
   int dma_row[C::DMA], dma_col[C::DMA];
 #pragma unroll
@@ -374,10 +459,10 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   auto step_q0 = [&](int s) __attribute__((always_inline)) { return (q_first + s % per_head) * BQ; };
   auto issue_step = [&](int s) __attribute__((always_inline)) {
     const int hq = step_head(s), q0 = step_q0(s);
-    const char* qs = p.q + ((int64_t)b * p.Nq + q0) * q_row + (int64_t)hq * D * 2;
-    const char* os = p.dout + ((int64_t)b * p.Nq + q0) * q_row + (int64_t)hq * D * 2;
+    const char* qs = p.q + ((int64_t)sq.qrow0 + q0) * q_row + (int64_t)hq * D * 2;
+    const char* os = p.dout + ((int64_t)sq.qrow0 + q0) * q_row + (int64_t)hq * D * 2;
     const uint32_t st = dma_lds + (uint32_t)((s % NST) * C::TILE);
-    const int last = p.Nq - 1 - q0;  // rows past the end re-read the last query (P = 0 there)
+    const int last = sq.Nqb - 1 - q0;  // rows past the end re-read the last query (P = 0 there)
 #pragma unroll
     for (int jj = 0; jj < C::DMA; ++jj) {
       const uint32_t off = (uint32_t)(min(dma_row[jj], last) * (int)q_row + dma_col[jj]);
@@ -464,8 +549,14 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
       for (int i = 0; i < 8; ++i) {
         float pv = exp2_fast(sacc[qb][h + i] * p.c);
         if constexpr (MASK) {
-          const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
-          if (my_k > qm) pv = 0.f;  // causal: key j visible to query i iff j <= i
+          // key j visible to query i iff i + off - wl <= j <= i + off + wr
+          if constexpr (WIN) {
+            const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3) + sq.off;
+            if ((p.wl >= 0 && my_k < qm - p.wl) || (p.wr >= 0 && my_k > qm + p.wr)) pv = 0.f;
+          } else {  // top-left causal: j <= i
+            const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
+            if (my_k > qm) pv = 0.f;
+          }
         }
         pe[i] = pv;
         se[i] = pv * dpacc[qb][h + i];
@@ -503,15 +594,27 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
     wait_vmcnt<0>();
     barrier();  // everyone's loads of step s landed; step s-1 is no longer read
     if (s + 1 < nsteps) issue_step(s + 1);
-    // a step needs the causal mask when some of its queries precede some of
-    // this wavefront's keys
-    const int q0 = step_q0(s);
-    if (p.causal && q0 < kw0 + 31) compute_step(s, std::true_type{});
-    else compute_step(s, std::false_type{});
+    // a step needs the mask unless every (query, key) pair of its queries
+    // and this wavefront's keys is visible (queries past the sequence have
+    // P = 0 through their -inf log-sum-exp)
+    // (written as one condition per path: other equivalent forms measured
+    // 5-8% slower in the dense kernel, the compiler allocating its
+    // registers differently)
+    if constexpr (WIN) {
+      const int q0 = step_q0(s) + sq.off;
+      if ((p.wl >= 0 && kw0 < q0 + BQ - 1 - p.wl) || (p.wr >= 0 && kw0 + 31 > q0 + p.wr))
+        compute_step(s, std::true_type{});
+      else
+        compute_step(s, std::false_type{});
+    } else {
+      const int q0 = step_q0(s);
+      if (p.wr >= 0 && q0 < kw0 + 31) compute_step(s, std::true_type{});
+      else compute_step(s, std::false_type{});
+    }
   }
 
-  if (my_k < p.Nk) {
-    const int64_t off = ((int64_t)b * p.Nk + my_k) * kv_row + (int64_t)kvh * D * 2;
+  if (my_k < sq.Nkb) {
+    const int64_t off = ((int64_t)sq.krow0 + my_k) * kv_row + (int64_t)kvh * D * 2;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -555,13 +658,24 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   p.Hkv = a.Hkv;
   p.group = a.Hq / a.Hkv;
   p.B = a.B;
-  p.causal = a.causal;
+  p.wl = a.window_left;
+  p.wr = a.window_right;
+  p.bottom_right = a.bottom_right;
+  p.lpt = a.window_right >= 0;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.total_q = a.total_q;
+  p.total_k = a.total_k;
   p.nq_pad = (a.Nq + kQStep - 1) / kQStep * kQStep;
   p.c = a.scale * kLog2e;
   p.scale = a.scale;
   p.dvec = static_cast<float*>(a.workspace);
   p.nlse = p.dvec + (size_t)a.B * a.Hq * p.nq_pad;
 
+  // the general kernels for windows other than top-left causal / none, and
+  // for packed batches
+  const bool win = a.cu_q != nullptr || a.bottom_right != 0 || a.window_left >= 0 ||
+                   (a.window_right != 0 && a.window_right != -1);
   const int64_t rows = (int64_t)a.B * a.Hq * p.nq_pad;
   if (rows > 0) {
     constexpr int RPB = 256 / (D / 8);
@@ -570,17 +684,25 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   using QC = DqCfg<D, 32>;
   const int n_qtiles = (a.Nq + QC::BM - 1) / QC::BM;
   if (n_qtiles > 0) {
-    hipLaunchKernelGGL((bwd_dq_kernel<QC>), dim3(n_qtiles * a.Hq * a.B), dim3(QC::THREADS), 0, stream, p, n_qtiles);
+    if (win)
+      hipLaunchKernelGGL((bwd_dq_kernel<QC, true>), dim3(n_qtiles * a.Hq * a.B), dim3(QC::THREADS), 0, stream, p,
+                         n_qtiles);
+    else
+      hipLaunchKernelGGL((bwd_dq_kernel<QC, false>), dim3(n_qtiles * a.Hq * a.B), dim3(QC::THREADS), 0, stream, p,
+                         n_qtiles);
   }
   using KC = DkvCfg<D>;
   const int n_ktiles = (a.Nk + KC::BK - 1) / KC::BK;
   if (n_ktiles > 0) {
     const dim3 grid(n_ktiles * a.Hkv * a.B);
     if (bwd_variant() == 1) {  // split pair: measured 9-15% slower on MI355X
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
     } else {
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      if (win)
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1, true>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      else
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
     }
   }
   return hipGetLastError();

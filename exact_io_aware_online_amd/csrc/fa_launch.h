@@ -65,10 +65,16 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  int B, Hq, Hkv, Nq, Nk, d;
-  int causal;
+  int B, Hq, Hkv, Nq, Nk, d;  // packed batches: Nq, Nk are the longest sequences
   float scale;
   void* workspace;  // >= bwd_workspace_bytes(B, Hq, Nq)
+  // visibility as in FwdArgs: i + off - window_left <= j <= i + off +
+  // window_right, off = Nk_b - Nq_b when bottom_right (top-left causal:
+  // window (-1, 0), bottom_right 0)
+  int window_left = -1, window_right = -1, bottom_right = 0;
+  const int32_t* cu_q = nullptr;  // packed variable-length batch, or null
+  const int32_t* cu_k = nullptr;
+  int total_q = 0, total_k = 0;
 };
 
 // FP8 (e4m3) forward: a bf16 tensor quantised per 64-row block of one

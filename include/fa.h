@@ -299,6 +299,30 @@ fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, c
                    int B, int Hq, int Hkv, int Nq, int Nk, int d, int causal, float scale,
                    void* workspace, size_t workspace_bytes, void* stream);
 
+/* fa_bwd under the visibility rule of fa_fwd_window (bottom-right aligned:
+ * key j is visible to query i iff i + off - window_left <= j <= i + off +
+ * window_right, off = Nk - Nq, a negative bound unlimited; causal is
+ * (-1, 0)). o and lse are those fa_fwd_window returned for the same window.
+ * Everything else (layouts, workspace, errors) is as fa_bwd. A query that
+ * sees no key gets dq = 0; a key no query sees gets dk = dv = 0. */
+fa_status_t fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          int B, int Hq, int Hkv, int Nq, int Nk, int d, int window_left, int window_right,
+                          float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* fa_bwd_window over a packed variable-length batch, the layouts of
+ * fa_fwd_varlen: q, o, dout, dq (total_q, Hq, d); k, v, dk, dv (total_k,
+ * Hkv, d); lse (Hq, total_q); cu_seqlens_q / cu_seqlens_k (B + 1,) int32 on
+ * the device. max_seqlen_q / max_seqlen_k bound the sequence lengths (longer
+ * sequences are cut there); the workspace is fa_bwd_workspace_size(B, Hq,
+ * max_seqlen_q) bytes. Offsets are clamped into the arrays. */
+fa_status_t fa_bwd_varlen(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                          const void* dout, void* dq, void* dk, void* dv,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int max_seqlen_q, int max_seqlen_k, int total_q, int total_k,
+                          int d, int window_left, int window_right, float scale,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
