@@ -205,3 +205,24 @@ def test_fp8_host_validation():
     assert fwd(q=null) == fa.FA_ERR_INVALID_ARG
     assert fwd(k=null) == fa.FA_ERR_INVALID_ARG
     assert fwd(k=null, Nk=0, q=null, Nq=0) == fa.FA_OK
+
+
+def test_backward_window_varlen_host_validation():
+    import ctypes
+    L = fa.lib()
+    null = None
+    fake = ctypes.c_void_p(64)  # never dereferenced: every case fails or ends before a launch
+    def win(d=128, Hq=4, B=1, q=fake, ws=null, ws_bytes=0):
+        return L.fa_bwd_window(q, fake, fake, fake, fake, fake, fake, fake, fake, B, Hq, 2, 64, 80, d, 10, 0, 0.1, ws,
+                               ws_bytes, null)
+    assert win(d=256) == fa.FA_ERR_UNSUPPORTED
+    assert win(Hq=3) == fa.FA_ERR_INVALID_ARG
+    assert win(q=null) == fa.FA_ERR_INVALID_ARG
+    assert win() == fa.FA_ERR_WORKSPACE
+    assert win(B=0) == fa.FA_OK
+    def var(cu=fake, total_q=100, B=2):
+        return L.fa_bwd_varlen(fake, fake, fake, fake, fake, fake, fake, fake, fake, cu, cu, B, 4, 2, 64, 64, total_q,
+                               90, 128, -1, 0, 0.1, null, 0, null)
+    assert var(cu=null) == fa.FA_ERR_INVALID_ARG
+    assert var() == fa.FA_ERR_WORKSPACE
+    assert var(B=0, cu=null) == fa.FA_OK
