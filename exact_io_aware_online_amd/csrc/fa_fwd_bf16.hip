@@ -367,21 +367,52 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     }
   };
 
-  // O^T += V^T P^T for tile t held in ring stage `stage`
+  // O^T += V^T P^T for tile t held in ring stage `stage`. Where registers
+  // allow (one query block, d <= 128), the V^T operands of the next
+  // 32-column block are read while the current block's MFMAs run (two
+  // register sets), so each MFMA waits on reads issued a block earlier
+  // rather than just before it.
   auto pv_phase = [&](int t, auto stage) __attribute__((always_inline)) {
     const uint32_t stg = (uint32_t)(int)stage * C::TILE_BYTES;
+    constexpr int NKK = BN / 16, NDT = D / 32;
+    constexpr bool AHEAD = QB == 1 && D <= 128;
+    i16x4 vr[AHEAD ? 2 : 1][NKK][2];
+    auto rd = [&](int dt, int buf) __attribute__((always_inline)) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int kk = 0; kk < BN / 16; ++kk) {
-        const i16x4 v0 = ds_read_tr(lds0 + stg + v_off[dt][0] + kk * 16 * D * 2);
-        const i16x4 v1 = ds_read_tr(lds0 + stg + v_off[dt][1] + kk * 16 * D * 2);
+        for (int h = 0; h < 2; ++h) vr[buf][kk][h] = ds_read_tr(lds0 + stg + v_off[dt][h] + kk * 16 * D * 2);
+    };
+    if constexpr (AHEAD) rd(0, 0);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      const int buf = AHEAD ? dt & 1 : 0;
+      if constexpr (AHEAD) {
+        if (dt + 1 < NDT) rd(dt + 1, (dt + 1) & 1);
+      } else {
+        rd(dt, 0);
+      }
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
         // registers 0..3: keys 4 g + r; 4..7: keys 8 + 4 g + r (of block kk)
+        const i16x4 v0 = vr[buf][kk][0], v1 = vr[buf][kk][1];
         const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
         const bf16x8 va = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][dt] = mfma32x32x16(va, pf[qb][kk], acc[qb][dt]);
       }
+    }
+    if constexpr (AHEAD) {
+      // issue order: the first block's reads, then each MFMA preceded by
+      // two reads of the next block
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * NKK, 0);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          if (dt + 1 < NDT) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        }
     }
   };
 
