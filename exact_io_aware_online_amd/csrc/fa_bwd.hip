@@ -506,8 +506,9 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acck[dt] = accv[dt] = f32x16{};
 
-  auto compute_step = [&](int s, auto mask_tag) __attribute__((always_inline)) {
-    constexpr bool MASK = decltype(mask_tag)::value;
+  // `masked`: some (query, key) pair of the step is invisible (a uniform
+  // flag: one copy of the step's code serves both cases)
+  auto compute_step = [&](int s, bool masked) __attribute__((always_inline)) {
     const int q0 = step_q0(s);
     const uint32_t qs = lds0 + (uint32_t)((s % NST) * C::TILE);
     const uint32_t os = qs + C::DO_REGION;
@@ -548,7 +549,7 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         float pv = exp2_fast(sacc[qb][h + i] * p.c);
-        if constexpr (MASK) {
+        if (masked) {
           // key j visible to query i iff i + off - wl <= j <= i + off + wr
           if constexpr (WIN) {
             const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3) + sq.off;
@@ -591,25 +592,25 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   };
 
   for (int s = 0; s < nsteps; ++s) {
+    // The dK and dV accumulators stay in AGPRs across steps: without this
+    // the compiler carries them in VGPRs and moves all 128 values in and
+    // out of AGPRs around every step's MFMAs.
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      asm volatile("" : "+a"(acck[dt]));
+      asm volatile("" : "+a"(accv[dt]));
+    }
     wait_vmcnt<0>();
     barrier();  // everyone's loads of step s landed; step s-1 is no longer read
     if (s + 1 < nsteps) issue_step(s + 1);
     // a step needs the mask unless every (query, key) pair of its queries
     // and this wavefront's keys is visible (queries past the sequence have
     // P = 0 through their -inf log-sum-exp)
-    // (written as one condition per path: other equivalent forms measured
-    // 5-8% slower in the dense kernel, the compiler allocating its
-    // registers differently)
     if constexpr (WIN) {
       const int q0 = step_q0(s) + sq.off;
-      if ((p.wl >= 0 && kw0 < q0 + BQ - 1 - p.wl) || (p.wr >= 0 && kw0 + 31 > q0 + p.wr))
-        compute_step(s, std::true_type{});
-      else
-        compute_step(s, std::false_type{});
+      compute_step(s, (p.wl >= 0 && kw0 < q0 + BQ - 1 - p.wl) || (p.wr >= 0 && kw0 + 31 > q0 + p.wr));
     } else {
-      const int q0 = step_q0(s);
-      if (p.wr >= 0 && q0 < kw0 + 31) compute_step(s, std::true_type{});
-      else compute_step(s, std::false_type{});
+      compute_step(s, p.wr >= 0 && step_q0(s) < kw0 + 31);
     }
   }
 
