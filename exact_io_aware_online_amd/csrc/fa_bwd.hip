@@ -365,9 +365,9 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
 // ---------------------------------------------------------------------------
 // 3. dK and dV: lane = key
 // ---------------------------------------------------------------------------
-template <int D_>
+template <int D_, int NST_ = 2>
 struct DkvCfg {
-  static constexpr int D = D_, NW = 4, BK = 128, THREADS = 256, NST = 2, BQ = kQStep, NQB = BQ / 32;
+  static constexpr int D = D_, NW = 4, BK = 128, THREADS = 256, NST = NST_, BQ = kQStep, NQB = BQ / 32;
   static constexpr int CPR = D / 8;
   static constexpr int TILE = BQ * D * 2;                 // one Q (or dO) tile
   static constexpr int DO_REGION = NST * TILE;
@@ -478,6 +478,7 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
           vec_lds + (uint32_t)((s % NST) * (C::NW * 1024)));
   };
   if (nsteps > 0) issue_step(0);
+  if (NST >= 3 && nsteps > 1) issue_step(1);
   wait_vm_loads();
 
   // LDS read offsets: Q and dO rows as A operands (b128), Q^T and dO^T
@@ -506,16 +507,21 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acck[dt] = accv[dt] = f32x16{};
 
-  // `masked`: some (query, key) pair of the step is invisible (a uniform
-  // flag: one copy of the step's code serves both cases)
-  auto compute_step = [&](int s, bool masked) __attribute__((always_inline)) {
-    const int q0 = step_q0(s);
-    const uint32_t qs = lds0 + (uint32_t)((s % NST) * C::TILE);
-    const uint32_t os = qs + C::DO_REGION;
-    const uint32_t vs = vec_lds + (uint32_t)((s % NST) * (C::NW * 1024));
-    // accumulator register i of query block qb holds query
-    // m = 32 qb + 8 (i / 4) + 4 g + i % 4 of the step
-    f32x16 sacc[C::NQB], dpacc[C::NQB];
+  // LDS stage bases as wave-uniform values: each read address is then one
+  // add of a per-lane offset plus an immediate
+  auto q_stage = [&](int s) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((s % NST) * C::TILE));
+  };
+  auto v_stage = [&](int s) __attribute__((always_inline)) {
+    return __builtin_amdgcn_readfirstlane(vec_lds + (uint32_t)((s % NST) * (C::NW * 1024)));
+  };
+
+  // S and dP accumulators of step s start at -LSE/scale and -D, so that
+  // after S = Q K^T and dP = dO V^T (query x key) they hold S - LSE/scale
+  // and dP - D. Register i of query block qb is query m = 32 qb + 8 (i / 4)
+  // + 4 g + i % 4 of the step.
+  auto sdp_init = [&](int s, f32x16* sacc, f32x16* dpacc) __attribute__((always_inline)) {
+    const uint32_t vs = v_stage(s);
 #pragma unroll
     for (int qb = 0; qb < C::NQB; ++qb)
 #pragma unroll
@@ -524,54 +530,71 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
         const f32x4 dd = *(const LDS3 f32x4*)(uintptr_t)(vs + BQ * 4 + (32 * qb + 8 * q4 + 4 * g) * 4);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sacc[qb][4 * q4 + e] = nl[e];    // S - LSE / scale after the products
-          dpacc[qb][4 * q4 + e] = -dd[e];  // dP - D after the products
+          sacc[qb][4 * q4 + e] = nl[e];
+          dpacc[qb][4 * q4 + e] = -dd[e];
         }
       }
-    // S = Q K^T and dP = dO V^T, query x key
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-#pragma unroll
-      for (int qb = 0; qb < C::NQB; ++qb) {
-        const bf16x8 qa = *(const LDS3 bf16x8*)(uintptr_t)(qs + a_off[ks] + qb * 32 * D * 2);
-        sacc[qb] = mfma32x32x16(qa, kf[ks], sacc[qb]);
-        if constexpr (DK) {
-          const bf16x8 oa = *(const LDS3 bf16x8*)(uintptr_t)(os + a_off[ks] + qb * 32 * D * 2);
-          dpacc[qb] = mfma32x32x16(oa, vf[ks], dpacc[qb]);
-        }
-      }
-    // P and dS = P o (dP - D), packed as B operands over the query index
-    bf16x8 pf[BQ / 16], sf[BQ / 16];
-#pragma unroll
-    for (int kk = 0; kk < BQ / 16; ++kk) {
-      const int qb = kk >> 1, h = (kk & 1) * 8;
-      float pe[8], se[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        float pv = exp2_fast(sacc[qb][h + i] * p.c);
-        if (masked) {
-          // key j visible to query i iff i + off - wl <= j <= i + off + wr
-          if constexpr (WIN) {
-            const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3) + sq.off;
-            if ((p.wl >= 0 && my_k < qm - p.wl) || (p.wr >= 0 && my_k > qm + p.wr)) pv = 0.f;
-          } else {  // top-left causal: j <= i
-            const int qm = q0 + 32 * qb + 8 * ((h + i) >> 2) + 4 * g + ((h + i) & 3);
-            if (my_k > qm) pv = 0.f;
-          }
-        }
-        pe[i] = pv;
-        se[i] = pv * dpacc[qb][h + i];
-      }
-      u32x4 wp, ws;
-#pragma unroll
-      for (int e2 = 0; e2 < 4; ++e2) {
-        wp[e2] = pack_bf16x2(pe[2 * e2], pe[2 * e2 + 1]);
-        ws[e2] = pack_bf16x2(se[2 * e2], se[2 * e2 + 1]);
-      }
-      pf[kk] = __builtin_bit_cast(bf16x8, wp);
-      sf[kk] = __builtin_bit_cast(bf16x8, ws);
+  };
+  // the S/dP MFMAs of a step in order j = 2 (ks NQB + qb) + (0: S, 1: dP)
+  constexpr int NSDP = 2 * C::NQB * (D / 16);
+  auto sdp_operand = [&](uint32_t qs, int j) __attribute__((always_inline)) {
+    const int ks = (j >> 1) / C::NQB, qb = (j >> 1) % C::NQB;
+    return *(const LDS3 bf16x8*)(uintptr_t)(qs + ((j & 1) ? C::DO_REGION : 0) + a_off[ks] + qb * 32 * D * 2);
+  };
+  auto sdp_mfma = [&](int j, const bf16x8& a, f32x16* sacc, f32x16* dpacc) __attribute__((always_inline)) {
+    const int ks = (j >> 1) / C::NQB, qb = (j >> 1) % C::NQB;
+    if (j & 1) {
+      if constexpr (DK) dpacc[qb] = mfma32x32x16(a, vf[ks], dpacc[qb]);
+    } else {
+      sacc[qb] = mfma32x32x16(a, kf[ks], sacc[qb]);
     }
-    // dV^T += dO^T P and dK^T += Q^T dS, d x key
+  };
+
+  // P/dS of step s. Key j is visible to query i iff i + off - wl <= j <=
+  // i + off + wr. With query i = q0 + c + 4 g, c the compile-time part of
+  // each register, that is x_lo >= c >= ... <= x_hi below; when the step
+  // needs no mask both bounds sit 2^30 keys away and never bind (sequences
+  // stay below 2^30 rows), so the test is branch-free.
+  struct Bounds { int x_hi, x_lo; };
+  auto step_bounds = [&](int s) __attribute__((always_inline)) {
+    bool masked;
+    if constexpr (WIN) {
+      const int q0 = step_q0(s) + sq.off;
+      masked = (p.wl >= 0 && kw0 < q0 + BQ - 1 - p.wl) || (p.wr >= 0 && kw0 + 31 > q0 + p.wr);
+    } else {
+      masked = p.wr >= 0 && step_q0(s) < kw0 + 31;
+    }
+    constexpr int kFar = 1 << 30;
+    const int lo = masked && p.wl >= 0 ? min(p.wl, kFar) : kFar;
+    const int hi = masked && p.wr >= 0 ? min(p.wr, kFar) : kFar;
+    const int qbase = step_q0(s) + (WIN ? sq.off : 0);
+    const int kx = my_k - 4 * g;
+    return Bounds{kx - (qbase + hi), kx - (qbase - lo)};  // invisible iff x_hi > c or x_lo < c
+  };
+  // element idx of the BQ x 32 / 64 P and dS values of this lane: P =
+  // 2^(c (S - LSE/scale)), dS = P o (dP - D), packed by pairs into the B
+  // operands pw (P) and sw (dS) over the query index
+  constexpr int NE = (BQ / 16) * 8;
+  auto pds_elem = [&](int idx, const f32x16* sacc, const f32x16* dpacc, Bounds bd, float& pe_prev, float& se_prev,
+                      u32x4* pw, u32x4* sw) __attribute__((always_inline)) {
+    const int kk = idx >> 3, i = idx & 7, qb = kk >> 1, h = (kk & 1) * 8;
+    float pv = exp2_fast(sacc[qb][h + i] * p.c);
+    const int c = 32 * qb + 8 * ((h + i) >> 2) + ((h + i) & 3);  // a constant after unrolling
+    if (bd.x_hi > c || (WIN && bd.x_lo < c)) pv = 0.f;
+    float sv = pv * dpacc[qb][h + i];
+    asm volatile("" : "+v"(pv), "+v"(sv));  // computed here, not moved towards its use
+    if (i & 1) {
+      pw[kk][i >> 1] = pack_bf16x2(pe_prev, pv);
+      sw[kk][i >> 1] = pack_bf16x2(se_prev, sv);
+    } else {
+      pe_prev = pv;
+      se_prev = sv;
+    }
+  };
+  // dV^T += dO^T P and dK^T += Q^T dS (d x key) for step s
+  auto dvdk = [&](int s, const u32x4* pw, const u32x4* sw) __attribute__((always_inline)) {
+    const uint32_t qs = q_stage(s);
+    const uint32_t os = qs + C::DO_REGION;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -580,37 +603,111 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
           const i16x4 o0 = ds_read_tr(os + t_off[dt][0] + kk * 16 * D * 2);
           const i16x4 o1 = ds_read_tr(os + t_off[dt][1] + kk * 16 * D * 2);
           const i16x8 ov = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-          accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), pf[kk], accv[dt]);
+          accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), __builtin_bit_cast(bf16x8, pw[kk]), accv[dt]);
         }
         if constexpr (DK) {
           const i16x4 q0v = ds_read_tr(qs + t_off[dt][0] + kk * 16 * D * 2);
           const i16x4 q1v = ds_read_tr(qs + t_off[dt][1] + kk * 16 * D * 2);
           const i16x8 qv = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-          acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), sf[kk], acck[dt]);
+          acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), __builtin_bit_cast(bf16x8, sw[kk]), acck[dt]);
         }
       }
   };
 
-  for (int s = 0; s < nsteps; ++s) {
-    // The dK and dV accumulators stay in AGPRs across steps: without this
-    // the compiler carries them in VGPRs and moves all 128 values in and
-    // out of AGPRs around every step's MFMAs.
+  // One step's products in issue order. Step `cs` (if >= 0) has its S/dP in
+  // csa/cdp: its P/dS and dV/dK are computed. Step `ns` (if >= 0) gets its
+  // S/dP into nsa/ndp, each of those MFMAs followed by a share of step cs's
+  // P/dS arithmetic, which the MFMA's execution then hides (one wavefront
+  // per SIMD has no other wavefront to fill its matrix pipe).
+  auto step_ops = [&](int cs, const f32x16* csa, const f32x16* cdp, int ns, f32x16* nsa, f32x16* ndp,
+                      auto has_cur, auto has_next) __attribute__((always_inline)) {
+    constexpr bool CUR = decltype(has_cur)::value, NXT = decltype(has_next)::value;
+    constexpr int PF = 4;                      // operand reads ahead of their MFMA
+    constexpr int EPM = (NE + NSDP - 1) / NSDP;  // P/dS elements after each MFMA
+    bf16x8 opr[NSDP];
+    uint32_t nqs = 0;
+    if constexpr (NXT) {
+      sdp_init(ns, nsa, ndp);
+      nqs = q_stage(ns);
+#pragma unroll
+      for (int j = 0; j < PF; ++j) opr[j] = sdp_operand(nqs, j);
+    }
+    Bounds bd{0, 0};
+    if constexpr (CUR) bd = step_bounds(cs);
+    u32x4 pw[BQ / 16], sw[BQ / 16];
+    float pe_prev = 0.f, se_prev = 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < (NXT ? NSDP : 1); ++j) {
+      if constexpr (NXT) {
+        if (j + PF < NSDP) opr[j + PF] = sdp_operand(nqs, j + PF);
+        sdp_mfma(j, opr[j], nsa, ndp);
+      }
+      if constexpr (CUR) {
+#pragma unroll
+        for (int e = 0; e < (NXT ? EPM : NE); ++e) {
+          const int idx = (NXT ? j * EPM : 0) + e;
+          if (idx < NE) pds_elem(idx, csa, cdp, bd, pe_prev, se_prev, pw, sw);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (CUR) dvdk(cs, pw, sw);
+  };
+
+  // The dK and dV accumulators stay in AGPRs across steps: without this the
+  // compiler carries them in VGPRs and moves all 128 values in and out of
+  // AGPRs around every step's MFMAs.
+  auto pin_acc = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       asm volatile("" : "+a"(acck[dt]));
       asm volatile("" : "+a"(accv[dt]));
     }
-    wait_vmcnt<0>();
-    barrier();  // everyone's loads of step s landed; step s-1 is no longer read
-    if (s + 1 < nsteps) issue_step(s + 1);
-    // a step needs the mask unless every (query, key) pair of its queries
-    // and this wavefront's keys is visible (queries past the sequence have
-    // P = 0 through their -inf log-sum-exp)
-    if constexpr (WIN) {
-      const int q0 = step_q0(s) + sq.off;
-      compute_step(s, (p.wl >= 0 && kw0 < q0 + BQ - 1 - p.wl) || (p.wr >= 0 && kw0 + 31 > q0 + p.wr));
-    } else {
-      compute_step(s, p.wr >= 0 && step_q0(s) < kw0 + 31);
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  f32x16 sa0[C::NQB], dp0[C::NQB];
+  if constexpr (NST >= 3) {
+    // Software pipeline over a three-stage ring: the S/dP MFMAs of step
+    // s + 1 run interleaved with the P/dS arithmetic of step s. Two sets
+    // of S/dP accumulators alternate between even and odd steps.
+    f32x16 sa1[C::NQB], dp1[C::NQB];
+    if (nsteps > 0) {
+      barrier();  // everyone's loads of steps 0 and 1 landed
+      step_ops(-1, sa1, dp1, 0, sa0, dp0, F_{}, T_{});
+    }
+    // step s with s + 1 < nsteps, PAR = s % 2
+    auto pipe_step = [&](int s, auto par) __attribute__((always_inline)) {
+      pin_acc();
+      wait_vmcnt<0>();
+      barrier();  // everyone's loads of step s + 1 landed; step s - 1 is no longer read
+      if (s + 2 < nsteps) issue_step(s + 2);
+      if constexpr (decltype(par)::value == 0) step_ops(s, sa0, dp0, s + 1, sa1, dp1, T_{}, T_{});
+      else step_ops(s, sa1, dp1, s + 1, sa0, dp0, T_{}, T_{});
+    };
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+      pipe_step(s, std::integral_constant<int, 0>{});
+      pipe_step(s + 1, std::integral_constant<int, 1>{});
+    }
+    if (s + 1 < nsteps) {
+      pipe_step(s, std::integral_constant<int, 0>{});
+      ++s;
+    }
+    if (s < nsteps) {  // the last step: its S/dP are in the set of its parity
+      pin_acc();
+      if (s & 1) step_ops(s, sa1, dp1, -1, sa0, dp0, T_{}, F_{});
+      else step_ops(s, sa0, dp0, -1, sa1, dp1, T_{}, F_{});
+    }
+  } else {
+    for (int s = 0; s < nsteps; ++s) {
+      pin_acc();
+      wait_vmcnt<0>();
+      barrier();  // everyone's loads of step s landed; step s-1 is no longer read
+      if (s + 1 < nsteps) issue_step(s + 1);
+      step_ops(-1, sa0, dp0, s, sa0, dp0, F_{}, T_{});
+      step_ops(s, sa0, dp0, -1, sa0, dp0, T_{}, F_{});
     }
   }
 
@@ -700,10 +797,11 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
       hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
       hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
     } else {
+      using KP = DkvCfg<D, 3>;  // pipelined: three-stage ring
       if (win)
-        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1, true>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KP, kDKDV, 1, true>), grid, dim3(KP::THREADS), 0, stream, p, n_ktiles);
       else
-        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDKDV, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KP, kDKDV, 1, false>), grid, dim3(KP::THREADS), 0, stream, p, n_ktiles);
     }
   }
   return hipGetLastError();
