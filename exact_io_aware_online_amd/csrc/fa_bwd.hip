@@ -591,27 +591,42 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
       se_prev = sv;
     }
   };
-  // dV^T += dO^T P and dK^T += Q^T dS (d x key) for step s
+  // dV^T += dO^T P and dK^T += Q^T dS (d x key) for step s: products m in
+  // the order (dt, kk, dV then dK), the transposed operand reads issued
+  // RA products ahead so each MFMA finds its operands in registers
   auto dvdk = [&](int s, const u32x4* pw, const u32x4* sw) __attribute__((always_inline)) {
     const uint32_t qs = q_stage(s);
     const uint32_t os = qs + C::DO_REGION;
+    constexpr int NKK = BQ / 16, W = (DV ? 1 : 0) + (DK ? 1 : 0), NOPS = (D / 32) * NKK * W, RA = 4;
+    i16x4 rt[NOPS][2];
+    auto is_dv = [&](int m) __attribute__((always_inline)) { return DV && (!DK || m % W == 0); };
+    auto rd = [&](int m) __attribute__((always_inline)) {
+      const int dt = m / (NKK * W), kk = (m / W) % NKK;
+      const uint32_t base = is_dv(m) ? os : qs;
+      rt[m][0] = ds_read_tr(base + t_off[dt][0] + kk * 16 * D * 2);
+      rt[m][1] = ds_read_tr(base + t_off[dt][1] + kk * 16 * D * 2);
+    };
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+    for (int m = 0; m < RA && m < NOPS; ++m) rd(m);
 #pragma unroll
-      for (int kk = 0; kk < BQ / 16; ++kk) {
-        if constexpr (DV) {
-          const i16x4 o0 = ds_read_tr(os + t_off[dt][0] + kk * 16 * D * 2);
-          const i16x4 o1 = ds_read_tr(os + t_off[dt][1] + kk * 16 * D * 2);
-          const i16x8 ov = {o0[0], o0[1], o0[2], o0[3], o1[0], o1[1], o1[2], o1[3]};
-          accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ov), __builtin_bit_cast(bf16x8, pw[kk]), accv[dt]);
-        }
-        if constexpr (DK) {
-          const i16x4 q0v = ds_read_tr(qs + t_off[dt][0] + kk * 16 * D * 2);
-          const i16x4 q1v = ds_read_tr(qs + t_off[dt][1] + kk * 16 * D * 2);
-          const i16x8 qv = {q0v[0], q0v[1], q0v[2], q0v[3], q1v[0], q1v[1], q1v[2], q1v[3]};
-          acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, qv), __builtin_bit_cast(bf16x8, sw[kk]), acck[dt]);
-        }
-      }
+    for (int m = 0; m < NOPS; ++m) {
+      if (m + RA < NOPS) rd(m + RA);
+      const int dt = m / (NKK * W), kk = (m / W) % NKK;
+      const i16x8 t = {rt[m][0][0], rt[m][0][1], rt[m][0][2], rt[m][0][3],
+                       rt[m][1][0], rt[m][1][1], rt[m][1][2], rt[m][1][3]};
+      if (is_dv(m))
+        accv[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), __builtin_bit_cast(bf16x8, pw[kk]), accv[dt]);
+      else
+        acck[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, t), __builtin_bit_cast(bf16x8, sw[kk]), acck[dt]);
+    }
+    // issue order: the first RA products' reads, then each MFMA preceded by
+    // the reads of the product RA later
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RA < NOPS ? RA : NOPS), 0);
+#pragma unroll
+    for (int m = 0; m < NOPS; ++m) {
+      if (m + RA < NOPS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
   };
 
   // One step's products in issue order. Step `cs` (if >= 0) has its S/dP in
