@@ -269,20 +269,38 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
 
   auto compute_tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
-    const uint32_t ks_base = lds0 + (uint32_t)((t % NST) * C::TILE);
+    // stage base as a wave-uniform value: one add per distinct lane offset
+    const uint32_t ks_base = __builtin_amdgcn_readfirstlane(lds0 + (uint32_t)((t % NST) * C::TILE));
     const uint32_t vs_base = ks_base + C::V_REGION;
     f32x16 s[NBT], dp[NBT];
 #pragma unroll
     for (int nb = 0; nb < NBT; ++nb) s[nb] = dp[nb] = f32x16{};
+    // S^T and dP^T products n = ks NBT + nb, their K and V operands read
+    // RS products ahead
+    {
+      constexpr int NP = (D / 16) * NBT, RS = 4;
+      bf16x8 ka[NP], va[NP];
+      auto rd = [&](int n) __attribute__((always_inline)) {
+        const int ks = n / NBT, nb = n % NBT;
+        ka[n] = *(const LDS3 bf16x8*)(uintptr_t)(ks_base + k_off[ks] + nb * 32 * D * 2);
+        va[n] = *(const LDS3 bf16x8*)(uintptr_t)(vs_base + k_off[ks] + nb * 32 * D * 2);
+      };
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+      for (int n = 0; n < RS && n < NP; ++n) rd(n);
 #pragma unroll
-      for (int nb = 0; nb < NBT; ++nb) {
-        const bf16x8 ka = *(const LDS3 bf16x8*)(uintptr_t)(ks_base + k_off[ks] + nb * 32 * D * 2);
-        const bf16x8 va = *(const LDS3 bf16x8*)(uintptr_t)(vs_base + k_off[ks] + nb * 32 * D * 2);
-        s[nb] = mfma32x32x16(ka, qf[ks], s[nb]);
-        dp[nb] = mfma32x32x16(va, of[ks], dp[nb]);
+      for (int n = 0; n < NP; ++n) {
+        if (n + RS < NP) rd(n + RS);
+        const int ks = n / NBT, nb = n % NBT;
+        s[nb] = mfma32x32x16(ka[n], qf[ks], s[nb]);
+        dp[nb] = mfma32x32x16(va[n], of[ks], dp[nb]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RS < NP ? RS : NP), 0);
+#pragma unroll
+      for (int n = 0; n < NP; ++n) {
+        if (n + RS < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    }
     // dS^T = P^T o (dP^T - D), P^T = 2^(c s - c LSE / scale); key
     // j0 + 4 g + o (o = 32 nb + 8 (i/4) + i%4) is visible iff lo <= o <= hi
     bf16x8 dsf[BN / 16];
@@ -311,16 +329,33 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
       for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(e[2 * e2], e[2 * e2 + 1]);
       dsf[kk] = __builtin_bit_cast(bf16x8, w);
     }
-    // dQ^T += K^T dS^T
+    // dQ^T += K^T dS^T, products m = dt (BN / 16) + kk, their transposed
+    // K^T operands read RA products ahead
+    {
+      constexpr int NKK = BN / 16, NP = (D / 32) * NKK, RA = 4;
+      i16x4 rt[NP][2];
+      auto rd = [&](int m) __attribute__((always_inline)) {
+        const int dt = m / NKK, kk = m % NKK;
+        rt[m][0] = ds_read_tr(ks_base + t_off[dt][0] + kk * 16 * D * 2);
+        rt[m][1] = ds_read_tr(ks_base + t_off[dt][1] + kk * 16 * D * 2);
+      };
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int m = 0; m < RA && m < NP; ++m) rd(m);
 #pragma unroll
-      for (int kk = 0; kk < BN / 16; ++kk) {
-        const i16x4 v0 = ds_read_tr(ks_base + t_off[dt][0] + kk * 16 * D * 2);
-        const i16x4 v1 = ds_read_tr(ks_base + t_off[dt][1] + kk * 16 * D * 2);
-        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      for (int m = 0; m < NP; ++m) {
+        if (m + RA < NP) rd(m + RA);
+        const int dt = m / NKK, kk = m % NKK;
+        const i16x8 vv = {rt[m][0][0], rt[m][0][1], rt[m][0][2], rt[m][0][3],
+                          rt[m][1][0], rt[m][1][1], rt[m][1][2], rt[m][1][3]};
         acc[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), dsf[kk], acc[dt]);
       }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (RA < NP ? RA : NP), 0);
+#pragma unroll
+      for (int m = 0; m < NP; ++m) {
+        if (m + RA < NP) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
   };
 
   auto sync_tile = [&](int t) __attribute__((always_inline)) {
