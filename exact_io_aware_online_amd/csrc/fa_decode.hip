@@ -345,20 +345,55 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int ro
   const int L = seq_len(p, b);
   const int n = (L + p.chunk - 1) / p.chunk;  // splits that hold keys
   const float* pl = p.part_lse + (int64_t)row * p.S;
-  float M = -INFINITY;
-  for (int s = lane; s < n; s += 64) M = fmaxf(M, pl[s]);
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-  const float Mu = (M == -INFINITY) ? 0.f : M;
   constexpr int PER = D / 64;
-  float o[PER > 0 ? PER : 1] = {};
-  float wsum = 0.f;
-  for (int s = 0; s < n; ++s) {
-    const float w = exp2_fast(pl[s] - Mu);
-    wsum += w;
-    const float* po = p.part_o + ((int64_t)row * p.S + s) * D;
+  // U splits at a time: every partial of a group is loaded before any is
+  // used, so a group costs one memory latency rather than U; indices past
+  // the last split re-read it and are not summed. The sums run in split order.
+  constexpr int U = 8;
+  float ls[U], po[U][PER];
+  auto load_group = [&](int s0) {
 #pragma unroll
-    for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[lane * PER + e], o[e]);
+    for (int u = 0; u < U; ++u) {
+      const int s = min(s0 + u, n - 1);
+      ls[u] = pl[s];
+      const float* src = p.part_o + ((int64_t)row * p.S + s) * D + lane * PER;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) po[u][e] = src[e];
+    }
+  };
+  float o[PER] = {};
+  float wsum = 0.f;
+  auto add_group = [&](int s0, float Mu) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (s0 + u < n) {
+        const float w = exp2_fast(ls[u] - Mu);
+        wsum += w;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[u][e], o[e]);
+      }
+    }
+  };
+  float M = -INFINITY;
+  if (n <= U) {
+    // the common case: one group, whose log-sum-exps give the maximum
+    if (n > 0) load_group(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (u < n) M = fmaxf(M, ls[u]);
+  } else {
+    for (int s = lane; s < n; s += 64) M = fmaxf(M, pl[s]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  }
+  const float Mu = (M == -INFINITY) ? 0.f : M;
+  if (n <= U) {
+    if (n > 0) add_group(0, Mu);
+  } else {
+    for (int s0 = 0; s0 < n; s0 += U) {
+      load_group(s0);
+      add_group(s0, Mu);
+    }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
