@@ -487,30 +487,61 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   }
   for (; t < ntiles; ++t) sync_tile(t);
 
-  // ---- epilogue: combine the two lane halves' sums, normalise once
+  // ---- epilogue: combine the two lane halves' sums, normalise once. At
+  // d = 64 and 128 (where the ring has room) the normalised rows go through
+  // LDS, idle now, so that each store writes whole rows: 16 lanes x 16
+  // bytes per row at d = 128, instead of 8-byte pieces of 32 rows per
+  // instruction. Those stores are non-temporal: O is written once and never
+  // read here, so its lines go to memory now rather than sitting dirty in
+  // the caches until a later kernel's traffic evicts them. At d = 256
+  // staging costs registers the kernel does not have; there the rows are
+  // stored from the accumulators as ordinary stores (partial lines written
+  // past the caches are slow).
+  constexpr int ROWB = D * 2;        // bytes of one O row
+  constexpr int WROWS = 32 * QB;     // rows of this wavefront
+  constexpr bool STAGE_O = D <= 128 && C::NW * WROWS * ROWB <= NST * C::STAGE_BYTES;
+  const uint32_t ost = lds0 + (uint32_t)(wave * WROWS * ROWB);
+  // 16-byte chunk c of row r sits at chunk c ^ (r % CPR), which spreads the
+  // writes below (one chunk of 32 rows per instruction) over the banks
+  if constexpr (STAGE_O) barrier();  // every wavefront is done reading the ring
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int my_q = qw0 + qb * 32 + r32;
+    const int row = qb * 32 + r32;
+    const int my_q = qw0 + row;
     const float lt = halves_sum(l[qb]);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (my_q < Nqb) {
-      char* orow = p.o + ((int64_t)qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
+    char* orow = p.o + ((int64_t)qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) {
+    for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int d0 = dt * 32 + 8 * j + 4 * g;
-          u32x2 w;
-          w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
-          w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + d0 * 2) = w;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int c = dt * 4 + j;  // chunk of dims 8c .. 8c+7; this lane's half g holds 8c + 4g ..
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
+        if constexpr (STAGE_O)
+          *(LDS3 u32x2*)(uintptr_t)(ost + row * ROWB + ((c ^ (row % CPR)) * 16) + g * 8) = w;
+        else if (my_q < Nqb)
+          *reinterpret_cast<u32x2*>(orow + c * 16 + g * 8) = w;
       }
-      if (p.lse != nullptr && g == 0) {
-        const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
-        p.lse[lrow + my_q] =
-            lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
-      }
+    }
+    if (p.lse != nullptr && g == 0 && my_q < Nqb) {
+      const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
+      p.lse[lrow + my_q] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
+    }
+  }
+  if constexpr (STAGE_O) {
+    // each wavefront reads back only its own rows: no barrier, the LDS
+    // instructions of one wavefront complete in order
+#pragma unroll
+    for (int i = 0; i < WROWS * CPR / 64; ++i) {
+      const int slot = i * 64 + lane;
+      const int row = slot / CPR, c = slot % CPR;
+      const u32x4 w = *(const LDS3 u32x4*)(uintptr_t)(ost + row * ROWB + ((c ^ (row % CPR)) * 16));
+      const int my_q = qw0 + row;
+      if (my_q < Nqb)
+        __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p.o + ((int64_t)qrow0 + my_q) * q_row +
+                                                                (int64_t)hq * D * 2 + c * 16));
     }
   }
 }
