@@ -382,18 +382,31 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
   }
   for (; t < ntiles; ++t) sync_tile(t);
 
-  if (my_q < sq.Nqb) {
-    char* row = p.dq + ((int64_t)sq.qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
+  // dQ rows go through the idle LDS ring so that 16-byte lanes store whole
+  // rows (non-temporal: written once, not read here)
+  static_assert(C::NW * 32 * D * 2 <= 2 * NST * C::TILE, "dQ staging exceeds the ring");
+  const uint32_t ost = lds0 + (uint32_t)(wave * 32 * D * 2);
+  barrier();  // every wavefront is done reading the ring
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+  for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = dt * 32 + 8 * jj + 4 * g;
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[dt][4 * jj + 0] * p.scale, acc[dt][4 * jj + 1] * p.scale);
-        w[1] = pack_bf16x2(acc[dt][4 * jj + 2] * p.scale, acc[dt][4 * jj + 3] * p.scale);
-        *reinterpret_cast<u32x2*>(row + d0 * 2) = w;
-      }
+    for (int jj = 0; jj < 4; ++jj) {
+      const int c = dt * 4 + jj;  // 16-byte chunk of dims 8c .. 8c+7; half g holds 8c + 4g ..
+      u32x2 w;
+      w[0] = pack_bf16x2(acc[dt][4 * jj + 0] * p.scale, acc[dt][4 * jj + 1] * p.scale);
+      w[1] = pack_bf16x2(acc[dt][4 * jj + 2] * p.scale, acc[dt][4 * jj + 3] * p.scale);
+      *(LDS3 u32x2*)(uintptr_t)(ost + r32 * D * 2 + ((c ^ (r32 % CPR)) * 16) + g * 8) = w;
+    }
+  // a wavefront reads back only its own rows (its LDS instructions complete in order)
+#pragma unroll
+  for (int i = 0; i < 32 * CPR / 64; ++i) {
+    const int slot = i * 64 + lane;
+    const int rw = slot / CPR, c = slot % CPR;
+    const u32x4 w = *(const LDS3 u32x4*)(uintptr_t)(ost + rw * D * 2 + ((c ^ (rw % CPR)) * 16));
+    const int q = qw0 + rw;
+    if (q < sq.Nqb)
+      __builtin_nontemporal_store(
+          w, reinterpret_cast<u32x4*>(p.dq + ((int64_t)sq.qrow0 + q) * q_row + (int64_t)hq * D * 2 + c * 16));
   }
 }
 
@@ -761,22 +774,37 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
     }
   }
 
-  if (my_k < sq.Nkb) {
-    const int64_t off = ((int64_t)sq.krow0 + my_k) * kv_row + (int64_t)kvh * D * 2;
+  // dK and dV rows go, one after the other, through the idle LDS so that
+  // 16-byte lanes store whole rows (non-temporal: written once, not read here)
+  static_assert(C::NW * 32 * D * 2 <= C::LDS_BYTES, "dK/dV staging exceeds the LDS");
+  const uint32_t ost = lds0 + (uint32_t)(wave * 32 * D * 2);
+  auto store_rows = [&](const f32x16 (&a)[D / 32], float mul, char* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
-        const int d0 = dt * 32 + 8 * jj + 4 * g;
-        u32x2 wk, wv;
-        wk[0] = pack_bf16x2(acck[dt][4 * jj + 0] * p.scale, acck[dt][4 * jj + 1] * p.scale);
-        wk[1] = pack_bf16x2(acck[dt][4 * jj + 2] * p.scale, acck[dt][4 * jj + 3] * p.scale);
-        wv[0] = pack_bf16x2(accv[dt][4 * jj + 0], accv[dt][4 * jj + 1]);
-        wv[1] = pack_bf16x2(accv[dt][4 * jj + 2], accv[dt][4 * jj + 3]);
-        if constexpr (DK) *reinterpret_cast<u32x2*>(p.dk + off + d0 * 2) = wk;
-        if constexpr (DV) *reinterpret_cast<u32x2*>(p.dv + off + d0 * 2) = wv;
+        const int c = dt * 4 + jj;  // 16-byte chunk of dims 8c .. 8c+7; half g holds 8c + 4g ..
+        u32x2 w;
+        w[0] = pack_bf16x2(a[dt][4 * jj + 0] * mul, a[dt][4 * jj + 1] * mul);
+        w[1] = pack_bf16x2(a[dt][4 * jj + 2] * mul, a[dt][4 * jj + 3] * mul);
+        *(LDS3 u32x2*)(uintptr_t)(ost + r32 * D * 2 + ((c ^ (r32 % CPR)) * 16) + g * 8) = w;
       }
-  }
+    // a wavefront reads back only its own rows (its LDS instructions
+    // complete in order, also against the next call's writes)
+#pragma unroll
+    for (int i = 0; i < 32 * CPR / 64; ++i) {
+      const int slot = i * 64 + lane;
+      const int rw = slot / CPR, c = slot % CPR;
+      const u32x4 w = *(const LDS3 u32x4*)(uintptr_t)(ost + rw * D * 2 + ((c ^ (rw % CPR)) * 16));
+      const int k = kw0 + rw;
+      if (k < sq.Nkb)
+        __builtin_nontemporal_store(
+            w, reinterpret_cast<u32x4*>(dst + ((int64_t)sq.krow0 + k) * kv_row + (int64_t)kvh * D * 2 + c * 16));
+    }
+  };
+  barrier();  // every wavefront is done reading the ring
+  if constexpr (DK) store_rows(acck, p.scale, p.dk);
+  if constexpr (DV) store_rows(accv, 1.f, p.dv);
 }
 
 // Kernel-shape override for tuning (FA_BWD_VARIANT), read once per process.
