@@ -181,23 +181,69 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     }
   };
 
-  // start the pipeline before loading Q
+  // ---- Q^T as B operand: register i of k-step ks = Q[row][16 ks + 8 g + i].
+  // At d = 128, where the ring stage that is still free holds the tile's BM
+  // query rows (BM <= 2 BN), they come in whole rows by direct-to-LDS
+  // loads, requested before the first K/V tiles, and each wavefront reads
+  // its operands from there (measured 2.3% faster on the short causal
+  // workload, 0.6% slower at d = 64); otherwise every lane loads its
+  // 16-byte pieces directly.
+  constexpr bool STAGE_Q = D == 128 && C::BM <= 2 * BN;
+  bf16x8 qf[QB][D / 16];
+  if constexpr (STAGE_Q) {
+    // rows [0, BN) of the tile into the K half of stage NST - 1, rows
+    // [BN, 2 BN) into its V half; rows past the sequence re-read its last
+    // query row (their operands are zeroed below)
+    const char* qbase = p.q + ((int64_t)qrow0 + q0) * q_row + (int64_t)hq * D * 2;
+    const int qlast = Nqb - 1 - q0;
+#pragma unroll
+    for (int h = 0; h < C::BM / BN; ++h) {
+      const uint32_t st = dma_lds + (uint32_t)((h ? C::V_REGION : 0) + (NST - 1) * C::TILE_BYTES);
+#pragma unroll
+      for (int j = 0; j < C::DMA; ++j)
+        dma16(qbase, (uint32_t)(min(h * BN + dma_row[j], qlast) * q_row + dma_col[j]), st + j * C::THREADS * 16);
+    }
+  }
+
+  // start the K/V pipeline
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < ntiles) issue_tile(s);
 
-  // ---- Q^T as B operand: register i of k-step ks = Q[row][16 ks + 8 g + i]
-  bf16x8 qf[QB][D / 16];
+  if constexpr (STAGE_Q) {
+    // own Q loads landed when at most the K/V tiles issued after them remain
+    const int issued = min(NST - 1, ntiles);
+    static_for<NST>([&](auto A) {
+      if (issued == decltype(A)::value) wait_vmcnt<decltype(A)::value * 2 * C::DMA>();
+    });
+    barrier();  // everyone's Q rows landed
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qw0 + qb * 32 + r32;
-    const char* qrow = p.q + ((int64_t)qrow0 + row) * q_row + (int64_t)hq * D * 2;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int trow = wave * 32 * QB + qb * 32 + r32;  // row within the tile
+      const int lrow = trow % BN;
+      const uint32_t base = lds0 + (uint32_t)((trow >= BN ? C::V_REGION : 0) + (NST - 1) * C::TILE_BYTES + lrow * D * 2);
+      const int sw = swz_pf<CPR>(lrow);
+      const bool valid = qw0 + qb * 32 + r32 < Nqb;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      qf[qb][ks] = row < Nqb ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const bf16x8 x = *(const LDS3 bf16x8*)(uintptr_t)(base + (((2 * ks + g) ^ sw) * 16));
+        qf[qb][ks] = valid ? x : bf16x8{};
+      }
     }
+    // the reads complete before the barrier after which tile NST - 1 refills this stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
+  } else {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = qw0 + qb * 32 + r32;
+      const char* qrow = p.q + ((int64_t)qrow0 + row) * q_row + (int64_t)hq * D * 2;
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        qf[qb][ks] = row < Nqb ? *reinterpret_cast<const bf16x8*>(qrow + (ks * 16 + g * 8) * 2) : bf16x8{};
+      }
+    }
+    wait_vm_loads();
   }
-  wait_vm_loads();
 
   f32x16 acc[QB][D / 32];
 #pragma unroll
