@@ -94,39 +94,61 @@ constexpr int kQStep = 32;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   constexpr int TPR = D / 8;        // threads per (b, i, h) row, 8 elements each
-  constexpr int RPB = 256 / TPR;    // rows per workgroup
-  // rows are indexed over (b, h, i) with i running to the padded length
-  const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / TPR;
+  constexpr int RPP = 256 / TPR;    // rows per pass of the workgroup
+  constexpr int U = 4;              // passes; every pass's loads are issued before any is used
+  // Rows run in memory order (b, i, h) with i up to the padded length, so
+  // the rows of a pass are adjacent heads of one query: contiguous bytes.
   const int part = threadIdx.x % TPR;
-  const int64_t total = (int64_t)p.B * p.Hq * p.nq_pad;
-  float acc = 0.f;
-  int i = 0, h = 0, b = 0;
-  Seq sq{0, 0, 0, 0, 0};
-  if (row < total) {
-    i = (int)(row % p.nq_pad);
-    const int64_t bh = row / p.nq_pad;
-    h = (int)(bh % p.Hq);
-    b = (int)(bh / p.Hq);
-    sq = seq_of<true>(p, b);
-    if (i < sq.Nqb) {
-      const int64_t off = (((int64_t)sq.qrow0 + i) * p.Hq + h) * D * 2 + part * 16;
-      const bf16x8 x = *reinterpret_cast<const bf16x8*>(p.dout + off);
-      const bf16x8 y = *reinterpret_cast<const bf16x8*>(p.o + off);
+  const int64_t total = (int64_t)p.B * p.nq_pad * p.Hq;
+  bf16x8 x[U], y[U];
+  int64_t orow[U];  // (b, h, i) index of the outputs; -1 past the end
+  int li_b[U], li_h[U], li_i[U];
+  bool live[U];     // a row of the sequence (not padding)
+  Seq sq[U];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+  for (int u = 0; u < U; ++u) {
+    const int64_t row = ((int64_t)blockIdx.x * U + u) * RPP + threadIdx.x / TPR;
+    orow[u] = -1;
+    live[u] = false;
+    li_b[u] = li_h[u] = li_i[u] = 0;
+    x[u] = y[u] = bf16x8{};
+    sq[u] = Seq{0, 0, 0, 0, 0};
+    if (row < total) {
+      const int h = (int)(row % p.Hq);
+      const int64_t bi = row / p.Hq;
+      const int i = (int)(bi % p.nq_pad);
+      const int b = (int)(bi / p.nq_pad);
+      sq[u] = seq_of<true>(p, b);
+      orow[u] = ((int64_t)b * p.Hq + h) * p.nq_pad + i;
+      li_b[u] = b;
+      li_h[u] = h;
+      li_i[u] = i;
+      if (i < sq[u].Nqb) {
+        live[u] = true;
+        const int64_t off = (((int64_t)sq[u].qrow0 + i) * p.Hq + h) * D * 2 + part * 16;
+        x[u] = *reinterpret_cast<const bf16x8*>(p.dout + off);
+        y[u] = *reinterpret_cast<const bf16x8*>(p.o + off);
+      }
     }
   }
 #pragma unroll
-  for (int w = TPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w, 64);
-  if (row < total && part == 0) {
-    float nl = -INFINITY;  // padded rows: P = 0
-    if (i < sq.Nqb) {
-      const int64_t li = p.cu_q != nullptr ? (int64_t)h * p.total_q + sq.qrow0 + i : ((int64_t)b * p.Hq + h) * p.Nq + i;
-      const float l = p.lse[li];
-      nl = l == -INFINITY ? -INFINITY : -l / p.scale;
+  for (int u = 0; u < U; ++u) {
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[u][e], (float)y[u][e], acc);
+#pragma unroll
+    for (int w = TPR / 2; w >= 1; w /= 2) acc += __shfl_xor(acc, w, 64);
+    if (orow[u] >= 0 && part == 0) {
+      float nl = -INFINITY;  // padded rows: P = 0
+      if (live[u]) {
+        const int64_t li = p.cu_q != nullptr ? (int64_t)li_h[u] * p.total_q + sq[u].qrow0 + li_i[u]
+                                              : ((int64_t)li_b[u] * p.Hq + li_h[u]) * p.Nq + li_i[u];
+        const float l = p.lse[li];
+        nl = l == -INFINITY ? -INFINITY : -l / p.scale;
+      }
+      p.dvec[orow[u]] = acc;
+      p.nlse[orow[u]] = nl;
     }
-    p.dvec[row] = acc;
-    p.nlse[row] = nl;
   }
 }
 
@@ -854,7 +876,7 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
                    (a.window_right != 0 && a.window_right != -1);
   const int64_t rows = (int64_t)a.B * a.Hq * p.nq_pad;
   if (rows > 0) {
-    constexpr int RPB = 256 / (D / 8);
+    constexpr int RPB = 4 * 256 / (D / 8);  // rows per workgroup: four passes
     hipLaunchKernelGGL((bwd_prep_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, p);
   }
   using QC = DqCfg<D, 32>;
