@@ -81,6 +81,20 @@ __device__ __forceinline__ int64_t cache_row(const DecParams& p, int b, int key)
   return (int64_t)page * p.page_size + (key - slot * p.page_size);
 }
 
+// The same for a key that is uniform across the wavefront. The page index
+// is read with a scalar load (constant address space), whose wait counts
+// in lgkmcnt: a vector load's wait (vmcnt) would also drain the
+// direct-to-LDS tile loads in flight.
+__device__ __forceinline__ int64_t cache_row_uniform(const DecParams& p, int b, int key) {
+  if (p.block_table == nullptr) return (int64_t)b * p.capacity + key;
+  const int slot = __builtin_amdgcn_readfirstlane(key / p.page_size);
+  const int64_t idx = (int64_t)__builtin_amdgcn_readfirstlane(b) * p.pages_per_seq + slot;
+  const __attribute__((address_space(4))) int32_t* bt =
+      (const __attribute__((address_space(4))) int32_t*)p.block_table;
+  const int page = min(max(bt[idx], 0), p.num_pages - 1);
+  return (int64_t)page * p.page_size + (key - slot * p.page_size);
+}
+
 // Tile shape: T keys per tile (a multiple of the 32-key MFMA step) and an
 // NST-stage ring; one K (or V) tile is T * D * 2 bytes, moved by
 // DMA = T * D * 2 / 1024 direct-to-LDS loads per lane.
@@ -166,7 +180,7 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
     const int last = end - start - 1 - j0;  // rows past the end re-read the last key (masked later)
     // a tile never straddles pages: page_size and the split starts are
     // multiples of the 64-key split alignment, tiles divide it
-    const int64_t row = cache_row(p, b, start + j0);
+    const int64_t row = cache_row_uniform(p, b, start + j0);
     const char* ks = p.kc + (row * p.Hkv + h) * D * 2;
     const char* vs = p.vc + (row * p.Hkv + h) * D * 2;
     const uint32_t st = lds0 + (uint32_t)((t % NST) * TL::STAGE);
