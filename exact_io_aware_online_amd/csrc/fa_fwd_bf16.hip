@@ -546,37 +546,33 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   constexpr int ROWB = D * 2;        // bytes of one O row
   constexpr int WROWS = 32 * QB;     // rows of this wavefront
   constexpr bool STAGE_O = D <= 128 && C::NW * WROWS * ROWB <= NST * C::STAGE_BYTES;
-  const uint32_t ost = lds0 + (uint32_t)(wave * WROWS * ROWB);
-  // 16-byte chunk c of row r sits at chunk c ^ (r % CPR), which spreads the
-  // writes below (one chunk of 32 rows per instruction) over the banks
-  if constexpr (STAGE_O) barrier();  // every wavefront is done reading the ring
+  if constexpr (STAGE_O) {
+    const uint32_t ost = lds0 + (uint32_t)(wave * WROWS * ROWB);
+    // 16-byte chunk c of row r sits at chunk c ^ (r % CPR), which spreads
+    // the writes below (one chunk of 32 rows per instruction) over the banks
+    barrier();  // every wavefront is done reading the ring
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    const int row = qb * 32 + r32;
-    const int my_q = qw0 + row;
-    const float lt = halves_sum(l[qb]);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    char* orow = p.o + ((int64_t)qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
+    for (int qb = 0; qb < QB; ++qb) {
+      const int row = qb * 32 + r32;
+      const int my_q = qw0 + row;
+      const float lt = halves_sum(l[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
+      for (int dt = 0; dt < D / 32; ++dt) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = dt * 4 + j;  // chunk of dims 8c .. 8c+7; this lane's half g holds 8c + 4g ..
-        u32x2 w;
-        w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
-        w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
-        if constexpr (STAGE_O)
+        for (int j = 0; j < 4; ++j) {
+          const int c = dt * 4 + j;  // chunk of dims 8c .. 8c+7; this lane's half g holds 8c + 4g ..
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
+          w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
           *(LDS3 u32x2*)(uintptr_t)(ost + row * ROWB + ((c ^ (row % CPR)) * 16) + g * 8) = w;
-        else if (my_q < Nqb)
-          *reinterpret_cast<u32x2*>(orow + c * 16 + g * 8) = w;
+        }
+      }
+      if (p.lse != nullptr && g == 0 && my_q < Nqb) {
+        const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
+        p.lse[lrow + my_q] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
       }
     }
-    if (p.lse != nullptr && g == 0 && my_q < Nqb) {
-      const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
-      p.lse[lrow + my_q] = lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
-    }
-  }
-  if constexpr (STAGE_O) {
     // each wavefront reads back only its own rows: no barrier, the LDS
     // instructions of one wavefront complete in order
 #pragma unroll
@@ -588,6 +584,34 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       if (my_q < Nqb)
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p.o + ((int64_t)qrow0 + my_q) * q_row +
                                                                 (int64_t)hq * D * 2 + c * 16));
+    }
+  } else {
+    // stores straight from the accumulators (this code shape keeps the
+    // d = 256 kernel's register allocation at its measured best)
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int my_q = qw0 + qb * 32 + r32;
+      const float lt = halves_sum(l[qb]);
+      const float inv = lt > 0.f ? 1.f / lt : 0.f;
+      if (my_q < Nqb) {
+        char* orow = p.o + ((int64_t)qrow0 + my_q) * q_row + (int64_t)hq * D * 2;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int d0 = dt * 32 + 8 * j + 4 * g;
+            u32x2 w;
+            w[0] = pack_bf16x2(acc[qb][dt][4 * j + 0] * inv, acc[qb][dt][4 * j + 1] * inv);
+            w[1] = pack_bf16x2(acc[qb][dt][4 * j + 2] * inv, acc[qb][dt][4 * j + 3] * inv);
+            *reinterpret_cast<u32x2*>(orow + d0 * 2) = w;
+          }
+        }
+        if (p.lse != nullptr && g == 0) {
+          const int64_t lrow = p.cu_q != nullptr ? (int64_t)hq * p.total_q + qrow0 : ((int64_t)b * p.Hq + hq) * p.Nq;
+          p.lse[lrow + my_q] =
+              lt > 0.f ? (m[qb] + log2_fast(lt)) * kLn2 : -INFINITY;
+        }
+      }
     }
   }
 }
