@@ -484,28 +484,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
   // here); d = 256 stores from the accumulators.
   constexpr int ROWB = D * 2, CPR = D / 8;
   constexpr bool STAGE_O = D <= 128 && C::NW * 32 * ROWB <= 2 * NST * C::TILE;
-  const uint32_t ost = lds0 + (uint32_t)(wave * 32 * ROWB);
   const int my_q = qw0 + r32;
   const float lt = halves_sum(l);
   const float inv = lt > 0.f ? (1.f / (1 << kPBias)) / lt : 0.f;
-  char* orow = p.o + (((int64_t)b * p.Nq + my_q) * p.Hq + hq) * D * 2;
-  if constexpr (STAGE_O) barrier();  // every wavefront is done reading the ring
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = dt * 4 + j;  // 16-byte chunk of dims 8c .. 8c+7; half g holds 8c + 4g ..
-      u32x2 w;
-      w[0] = pack_bf16x2(acc[dt][4 * j + 0] * inv, acc[dt][4 * j + 1] * inv);
-      w[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
-      if constexpr (STAGE_O)
-        *(LDS3 u32x2*)(uintptr_t)(ost + r32 * ROWB + ((c ^ (r32 % CPR)) * 16) + g * 8) = w;
-      else if (my_q < p.Nq)
-        *reinterpret_cast<u32x2*>(orow + c * 16 + g * 8) = w;
-    }
-  if (my_q < p.Nq && p.lse != nullptr && g == 0)
-    p.lse[qhead * p.Nq + my_q] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
   if constexpr (STAGE_O) {
+    const uint32_t ost = lds0 + (uint32_t)(wave * 32 * ROWB);
+    barrier();  // every wavefront is done reading the ring
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = dt * 4 + j;  // 16-byte chunk of dims 8c .. 8c+7; half g holds 8c + 4g ..
+        u32x2 w;
+        w[0] = pack_bf16x2(acc[dt][4 * j + 0] * inv, acc[dt][4 * j + 1] * inv);
+        w[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
+        *(LDS3 u32x2*)(uintptr_t)(ost + r32 * ROWB + ((c ^ (r32 % CPR)) * 16) + g * 8) = w;
+      }
+    if (my_q < p.Nq && p.lse != nullptr && g == 0)
+      p.lse[qhead * p.Nq + my_q] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
     // a wavefront reads back only its own rows (its LDS instructions complete in order)
 #pragma unroll
     for (int i = 0; i < 32 * CPR / 64; ++i) {
@@ -516,6 +512,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
       if (q < p.Nq)
         __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p.o + (((int64_t)b * p.Nq + q) * p.Hq + hq) * D * 2 +
                                                                 c * 16));
+    }
+  } else {
+    // stores straight from the accumulators, in the code shape the d = 256
+    // kernel's register allocation was measured with
+    if (my_q < p.Nq) {
+      char* orow = p.o + (((int64_t)b * p.Nq + my_q) * p.Hq + hq) * D * 2;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int d0 = dt * 32 + 8 * j + 4 * g;
+          u32x2 w;
+          w[0] = pack_bf16x2(acc[dt][4 * j + 0] * inv, acc[dt][4 * j + 1] * inv);
+          w[1] = pack_bf16x2(acc[dt][4 * j + 2] * inv, acc[dt][4 * j + 3] * inv);
+          *reinterpret_cast<u32x2*>(orow + d0 * 2) = w;
+        }
+      if (p.lse != nullptr && g == 0)
+        p.lse[qhead * p.Nq + my_q] = lt > 0.f ? (m + log2_fast(lt)) * kLn2 : -INFINITY;
     }
   }
 }
