@@ -1,0 +1,55 @@
+"""Host-side checks of bench.py's contract (no GPU): the one-GPU refusal,
+the algorithmic FLOP accounting of the metric, and that stored HBM traffic
+is reported only for the kernel source it was measured on."""
+
+import json
+import os
+import subprocess
+import sys
+
+import bench
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0
+    assert "one GPU" in r.stdout + r.stderr
+
+
+def test_prefill_flops_accounting():
+    # 4 B H Nq Nk d, halved for causal, as the metric states
+    w = dict(B=8, Hq=16, Nq=2048, Nk=2048, d=128, causal=True)
+    assert bench.prefill_flops(w) == 4 * 8 * 16 * 2048 * 2048 * 128 / 2
+    assert bench.prefill_flops(dict(w, causal=False)) == 4 * 8 * 16 * 2048 * 2048 * 128
+    # the headline workload: 137.44 GFLOP per launch
+    assert abs(bench.prefill_flops(w) / 1e9 - 137.44) < 0.01
+
+
+def test_stored_traffic_follows_the_source_hash(tmp_path, monkeypatch):
+    src = tmp_path / "kernel.hip"
+    src.write_text("kernel v1")
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"k": {"source_sha256_16": bench.source_hash([str(src)]), "bytes_per_launch": 123}}
+    (prof / "hbm_traffic.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.stored_traffic("k", [str(src)]) == 123
+    assert bench.stored_traffic("missing", [str(src)]) is None
+    src.write_text("kernel v2")  # the kernel changed since the counters were taken
+    assert bench.stored_traffic("k", [str(src)]) is None
+
+
+def test_committed_traffic_records_are_well_formed():
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json")) as f:
+        recs = json.load(f)
+    for key, rec in recs.items():
+        if key.startswith("_"):
+            continue
+        for field in ("kernel", "source_sha256_16", "fetch_kib", "write_kib", "fetch_factor", "write_factor",
+                      "bytes_per_launch"):
+            assert field in rec, (key, field)
+        expect = (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024
+        assert abs(rec["bytes_per_launch"] - expect) <= 1e-3 * expect + 1024, key
