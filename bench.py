@@ -94,14 +94,25 @@ def cpu_baseline(name, w, budget_s=12.0):
             break
     el = time.perf_counter() - t0
     per_head = prefill_flops(dict(w, B=1, Hq=1))
+    blas = "unknown"
     try:
         from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        cores = max([p.get("num_threads", 1) for p in pools] or [1])
+        if pools:
+            blas = f"{pools[0].get('internal_api', '?')} {pools[0].get('version', '')}".strip()
     except Exception:
         cores = os.cpu_count()
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next(l.split(":", 1)[1].strip() for l in f if l.startswith("model name"))
+    except (OSError, StopIteration):
+        pass
     return {"value": per_head * done / el / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{done} of {w['B'] * w['Hq']} (batch, head) slices of {name}, "
-                      f"full fp64 score matrix each, {el:.1f} s"}
+                      f"full fp64 score matrix each, {el:.1f} s",
+            "cpu": cpu, "blas": blas}
 
 
 def main():

@@ -53,3 +53,12 @@ def test_committed_traffic_records_are_well_formed():
             assert field in rec, (key, field)
         expect = (rec["fetch_kib"] * rec["fetch_factor"] + rec["write_kib"] * rec["write_factor"]) * 1024
         assert abs(rec["bytes_per_launch"] - expect) <= 1e-3 * expect + 1024, key
+
+
+def test_cpu_baseline_fields_on_a_tiny_workload():
+    w = dict(B=1, Hq=2, Hkv=1, Nq=64, Nk=64, d=64, causal=True, dtype="bf16", seed=1)
+    r = bench.cpu_baseline("tiny", w, budget_s=0.5)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
+    assert r["value"] > 0 and r["cores"] >= 1
+    assert "slices of tiny" in r["sample"]
+    assert isinstance(r["cpu"], str) and isinstance(r["blas"], str)
