@@ -75,7 +75,7 @@ def lib():
     L.fa_fwd_kvcache_workspace_size.restype = sz
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
     L.fa_kvcache_default_splits.restype = i
-    L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i]
+    L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i, i]
     L.fa_fwd_kvcache_paged.restype = i
     L.fa_fwd_kvcache_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_fwd_kvcache_append.restype = i
@@ -130,6 +130,22 @@ def _check(t, name, dtype=None, device=None):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if device is not None and t.device != device:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _shape(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _workspace(workspace, need, device):
+    """The caller's workspace (any dtype, contiguous, on `device`) or a new
+    one of `need` bytes; returns (tensor or None, its size in bytes)."""
+    import torch
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    if workspace is not None:
+        _check(workspace, "workspace", device=device)
+    return workspace, 0 if workspace is None else workspace.numel() * workspace.element_size()
 
 
 def fa_fwd(q, k, v, o=None, lse=None, causal=False, scale=None, stream=None, want_lse=True):
@@ -194,10 +210,12 @@ def fa_fwd_window(q, k, v, window_left=-1, window_right=-1, o=None, lse=None, sc
         _check(t, n, torch.bfloat16, q.device)
     o = torch.empty_like(q) if o is None else o
     _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q.device)
+        _shape(lse, (B, Hq, Nq), "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, Hq, Hkv, Nq, Nk, d,
@@ -227,14 +245,16 @@ def fa_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, window_left
     for t, n in ((cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
         _check(t, n, torch.int32, q.device)
     B = cu_seqlens_q.numel() - 1
-    if B < 0 or cu_seqlens_k.numel() != B + 1:
+    if B < 0 or cu_seqlens_q.dim() != 1 or tuple(cu_seqlens_k.shape) != (B + 1,):
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both be (B + 1,)")
     o = torch.empty_like(q) if o is None else o
     _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
     if lse is None and want_lse:
         lse = torch.empty((Hq, total_q), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q.device)
+        _shape(lse, (Hq, total_q), "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
@@ -249,8 +269,9 @@ def fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits):
     return int(lib().fa_fwd_kvcache_workspace_size(int(B), int(Hq), int(d), int(num_splits)))
 
 
-def fa_kvcache_default_splits(B, Hkv, capacity, num_cus=0, wgs_per_cu=0):
-    return int(lib().fa_kvcache_default_splits(int(B), int(Hkv), int(capacity), int(num_cus), int(wgs_per_cu)))
+def fa_kvcache_default_splits(B, Hkv, capacity, d=128, num_cus=0, wgs_per_cu=0):
+    return int(lib().fa_kvcache_default_splits(int(B), int(Hkv), int(capacity), int(d), int(num_cus),
+                                               int(wgs_per_cu)))
 
 
 def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_splits=None, scale=None,
@@ -275,18 +296,17 @@ def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_split
     if tuple(cache_seqlens.shape) != (B,):
         raise ValueError("cache_seqlens must be (B,)")
     if num_splits is None:
-        num_splits = fa_kvcache_default_splits(B, Hkv, cap)
+        num_splits = fa_kvcache_default_splits(B, Hkv, cap, d)
     if o is None:
         o = torch.empty_like(q)
     _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q.device)
-    need = fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _shape(lse, (B, Hq), "lse")
+    workspace, ws_bytes = _workspace(workspace, fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_kvcache(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
@@ -320,18 +340,17 @@ def fa_fwd_kvcache_paged(q, kpages, vpages, block_table, cache_seqlens, o=None, 
         raise ValueError("block_table must be (B, pages_per_seq) and cache_seqlens (B,)")
     pages_per_seq = block_table.shape[1]
     if num_splits is None:
-        num_splits = fa_kvcache_default_splits(B, Hkv, page_size * pages_per_seq)
+        num_splits = fa_kvcache_default_splits(B, Hkv, page_size * pages_per_seq, d)
     if o is None:
         o = torch.empty_like(q)
     _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
     if lse is None and want_lse:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q.device)
-    need = fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _shape(lse, (B, Hq), "lse")
+    workspace, ws_bytes = _workspace(workspace, fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_kvcache_paged(_ptr(q), _ptr(kpages), _ptr(vpages), _ptr(block_table), _ptr(cache_seqlens),
@@ -361,18 +380,17 @@ def _append_common(q, k_new, v_new, cache_seqlens, Hkv, d, cap, o, lse, num_spli
     if tuple(cache_seqlens.shape) != (B,):
         raise ValueError("cache_seqlens must be (B,)")
     if num_splits is None:
-        num_splits = fa_kvcache_default_splits(B, Hkv, cap)
+        num_splits = fa_kvcache_default_splits(B, Hkv, cap, d)
     if o is None:
         o = torch.empty_like(q)
     _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q.device)
-    need = fa_fwd_kvcache_workspace_size(B * Nq, Hq, d, num_splits)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+        _shape(lse, (B, Hq, Nq), "lse")
+    workspace, ws_bytes = _workspace(workspace, fa_fwd_kvcache_workspace_size(B * Nq, Hq, d, num_splits), q.device)
     return B, Nq, Hq, o, lse, int(num_splits), workspace, ws_bytes
 
 
@@ -386,6 +404,9 @@ def fa_fwd_kvcache_append(q, kcache, vcache, cache_seqlens, k_new=None, v_new=No
     Returns (o (B, Nq, Hq, d) bf16, lse (B, Hq, Nq) float32).
     """
     import torch
+    if q.dim() != 4 or kcache.dim() != 4:
+        raise ValueError("q must be (batch, queries, heads, head_dim) and the caches (batch, capacity, heads, "
+                         "head_dim)")
     _, cap, Hkv, d = kcache.shape
     if tuple(vcache.shape) != tuple(kcache.shape) or kcache.shape[0] != q.shape[0]:
         raise ValueError("cache shapes do not match q")
@@ -490,13 +511,18 @@ def fa_fwd_fp8(q8, q_scales, k8, k_scales, vt8, v_scales, Nq, Nk, causal=False, 
     for t, n in ((q8, "q8"), (k8, "k8"), (vt8, "vt8"), (q_scales, "q_scales"), (k_scales, "k_scales"),
                  (v_scales, "v_scales")):
         _check(t, n, torch.uint8, q8.device)
+    _shape(q_scales, (B, Hq, Nqp // 64), "q_scales")
+    _shape(k_scales, (B, Hkv, fa_fp8_padded_rows(Nk) // 64), "k_scales")
+    _shape(v_scales, (B, Hkv, fa_fp8_padded_rows(Nk) // 64), "v_scales")
     if o is None:
         o = torch.empty((B, Nq, Hq, d), dtype=torch.bfloat16, device=q8.device)
     _check(o, "o", torch.bfloat16, q8.device)
+    _shape(o, (B, Nq, Hq, d), "o")
     if lse is None and want_lse:
         lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=q8.device)
     if lse is not None:
         _check(lse, "lse", torch.float32, q8.device)
+        _shape(lse, (B, Hq, Nq), "lse")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_fwd_fp8(_ptr(q8), _ptr(q_scales), _ptr(k8), _ptr(k_scales), _ptr(vt8), _ptr(v_scales), _ptr(o),
@@ -540,10 +566,7 @@ def fa_bwd(q, k, v, o, lse, dout, causal=False, scale=None, dq=None, dk=None, dv
         _check(t, n, torch.bfloat16, q.device)
         if tuple(t.shape) != tuple(ref.shape):
             raise ValueError(f"{n} must have the shape of {n[1:]}")
-    need = fa_bwd_workspace_size(B, Hq, Nq)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    workspace, ws_bytes = _workspace(workspace, fa_bwd_workspace_size(B, Hq, Nq), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
@@ -559,18 +582,24 @@ def fa_bwd_window(q, k, v, o, lse, dout, window_left, window_right, scale=None, 
     """Attention backward under a bottom-right aligned window through
     ``fa_bwd_window``; shapes as ``fa_bwd``. Returns (dq, dk, dv)."""
     import torch
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v must be (batch, seq, heads, head_dim)")
     B, Nq, Hq, d = q.shape
     _, Nk, Hkv, _ = k.shape
+    if tuple(k.shape) != (B, Nk, Hkv, d):
+        raise ValueError("k does not match q")
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check(t, n, torch.bfloat16, q.device)
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _shape(t, q.shape, n)
+    for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
+        _shape(t, k.shape, n)
     _check(lse, "lse", torch.float32, q.device)
-    need = fa_bwd_workspace_size(B, Hq, Nq)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _shape(lse, (B, Hq, Nq), "lse")
+    workspace, ws_bytes = _workspace(workspace, fa_bwd_workspace_size(B, Hq, Nq), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_bwd_window(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
@@ -587,21 +616,29 @@ def fa_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_
     q, o, dout (total_q, Hq, d), k, v (total_k, Hkv, d) bf16, lse (Hq,
     total_q) float32 as ``fa_fwd_varlen`` returns it. Returns (dq, dk, dv)."""
     import torch
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q, k, v must be (tokens, heads, head_dim)")
     total_q, Hq, d = q.shape
     total_k, Hkv, _ = k.shape
+    if k.shape[2] != d:
+        raise ValueError("k does not match q")
     B = cu_seqlens_q.shape[0] - 1
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"), (dk, "dk"), (dv, "dv")):
         _check(t, n, torch.bfloat16, q.device)
+    for t, n in ((o, "o"), (dout, "dout"), (dq, "dq")):
+        _shape(t, q.shape, n)
+    for t, n in ((v, "v"), (dk, "dk"), (dv, "dv")):
+        _shape(t, k.shape, n)
     _check(lse, "lse", torch.float32, q.device)
+    _shape(lse, (Hq, total_q), "lse")
     _check(cu_seqlens_q, "cu_seqlens_q", torch.int32, q.device)
     _check(cu_seqlens_k, "cu_seqlens_k", torch.int32, q.device)
-    need = fa_bwd_workspace_size(B, Hq, max_seqlen_q)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    if B < 0 or cu_seqlens_q.dim() != 1 or tuple(cu_seqlens_k.shape) != (B + 1,):
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be (B + 1,)")
+    workspace, ws_bytes = _workspace(workspace, fa_bwd_workspace_size(B, Hq, max_seqlen_q), q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     st = lib().fa_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),

@@ -15,7 +15,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
@@ -149,7 +149,7 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits) {
   return fa::decode_workspace_bytes(B, Hq, d, num_splits);
 }
 
-int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu) {
+int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu) {
   if (B <= 0 || Hkv <= 0 || capacity <= 0) return 1;
   if (num_cus <= 0) {
     int dev = 0;
@@ -160,7 +160,7 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs
       num_cus = 256;
     }
   }
-  if (wgs_per_cu <= 0) wgs_per_cu = 3;
+  if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_resident_per_cu(d);
   // Splits of about 1024 keys keep each decode wavefront's stream long
   // enough to amortise its pipeline start (measured best on MI355X against
   // 512 and 768), and enough of them give every CU `wgs_per_cu` resident

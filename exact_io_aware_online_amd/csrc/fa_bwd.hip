@@ -62,8 +62,12 @@ struct BwdParams {
 
 // One sequence's rows: where its queries and keys start in the (packed or
 // dense) arrays, how many there are, and the window offset.
+// A packed sequence longer than the launch covers (max_seqlen_q / _k) is
+// `bad`: its gradient rows are all written as NaN instead.
 struct Seq {
   int qrow0, Nqb, krow0, Nkb, off;
+  int lq, lk;  // the sequence's own lengths
+  bool bad;
 };
 
 template <bool WIN>
@@ -71,15 +75,18 @@ __device__ __forceinline__ Seq seq_of(const BwdParams& p, int b) {
   Seq s;
   if (WIN && p.cu_q != nullptr) {  // offsets clamped into the arrays
     s.qrow0 = min(max(p.cu_q[b], 0), p.total_q);
-    s.Nqb = min(min(max(p.cu_q[b + 1], s.qrow0), p.total_q) - s.qrow0, p.Nq);
+    s.lq = min(max(p.cu_q[b + 1], s.qrow0), p.total_q) - s.qrow0;
+    s.Nqb = min(s.lq, p.Nq);
     s.krow0 = min(max(p.cu_k[b], 0), p.total_k);
-    s.Nkb = min(min(max(p.cu_k[b + 1], s.krow0), p.total_k) - s.krow0, p.Nk);
+    s.lk = min(max(p.cu_k[b + 1], s.krow0), p.total_k) - s.krow0;
+    s.Nkb = min(s.lk, p.Nk);
   } else {
     s.qrow0 = b * p.Nq;
-    s.Nqb = p.Nq;
+    s.Nqb = s.lq = p.Nq;
     s.krow0 = b * p.Nk;
-    s.Nkb = p.Nk;
+    s.Nkb = s.lk = p.Nk;
   }
+  s.bad = s.lq > p.Nq || s.lk > p.Nk;
   s.off = WIN && p.bottom_right ? s.Nkb - s.Nqb : 0;
   return s;
 }
@@ -112,7 +119,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     live[u] = false;
     li_b[u] = li_h[u] = li_i[u] = 0;
     x[u] = y[u] = bf16x8{};
-    sq[u] = Seq{0, 0, 0, 0, 0};
+    sq[u] = Seq{0, 0, 0, 0, 0, 0, 0, false};
     if (row < total) {
       const int h = (int)(row % p.Hq);
       const int64_t bi = row / p.Hq;
@@ -194,6 +201,13 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
   const int q0 = qt * C::BM;
   const int qw0 = q0 + wave * 32;
   const Seq sq = seq_of<WIN>(p, b);
+  if constexpr (WIN) {
+    if (sq.bad) {  // the last query tile's workgroup also covers the rows past the grid
+      fill_nan_rows<D * 2>(p.dq + (int64_t)sq.qrow0 * p.Hq * D * 2 + (int64_t)hq * D * 2, (int64_t)p.Hq * D * 2,
+                           min(q0, sq.lq), qt == n_qtiles - 1 ? sq.lq : min(q0 + C::BM, sq.lq), tid, C::THREADS);
+      return;
+    }
+  }
   if (q0 >= sq.Nqb) return;  // whole workgroup: past this sequence's queries
 
   const int64_t q_row = (int64_t)p.Hq * D * 2;
@@ -477,6 +491,15 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   const int kw0 = k0 + wave * 32;     // first key of this wavefront
   const int my_k = kw0 + r32;         // this lane's key (MFMA column)
   const Seq sq = seq_of<WIN>(p, b);
+  if constexpr (WIN) {
+    if (sq.bad) {  // the last key tile's workgroup also covers the rows past the grid
+      const int r0 = min(k0, sq.lk), r1 = kt == n_ktiles - 1 ? sq.lk : min(k0 + C::BK, sq.lk);
+      const int64_t base = (int64_t)sq.krow0 * p.Hkv * D * 2 + (int64_t)kvh * D * 2;
+      if constexpr (DK) fill_nan_rows<D * 2>(p.dk + base, (int64_t)p.Hkv * D * 2, r0, r1, tid, C::THREADS);
+      if constexpr (DV) fill_nan_rows<D * 2>(p.dv + base, (int64_t)p.Hkv * D * 2, r0, r1, tid, C::THREADS);
+      return;
+    }
+  }
 
   const int kv_row = p.Hkv * D * 2;
   const int64_t q_row = (int64_t)p.Hq * D * 2;
@@ -829,13 +852,11 @@ __global__ __launch_bounds__(C::THREADS, WPS) void bwd_dkdv_kernel(BwdParams p, 
   if constexpr (DV) store_rows(accv, 1.f, p.dv);
 }
 
-// Kernel-shape override for tuning (FA_BWD_VARIANT), read once per process.
+// Kernel-shape override for tuning (FA_BWD_VARIANT=1: dK and dV in two
+// separate passes), read at every call.
 int bwd_variant() {
-  static const int v = [] {
-    const char* e = getenv("FA_BWD_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+  const char* e = getenv("FA_BWD_VARIANT");
+  return e ? atoi(e) : 0;
 }
 
 template <int D>
@@ -894,8 +915,13 @@ hipError_t launch(const BwdArgs& a, hipStream_t stream) {
   if (n_ktiles > 0) {
     const dim3 grid(n_ktiles * a.Hkv * a.B);
     if (bwd_variant() == 1) {  // split pair: measured 9-15% slower on MI355X
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
-      hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      if (win) {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2, true>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1, true>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      } else {
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDV, 2, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+        hipLaunchKernelGGL((bwd_dkdv_kernel<KC, kDK, 1, false>), grid, dim3(KC::THREADS), 0, stream, p, n_ktiles);
+      }
     } else {
       using KP = DkvCfg<D, 3>;  // pipelined: three-stage ring
       if (win)

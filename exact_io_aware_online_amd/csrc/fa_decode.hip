@@ -479,6 +479,19 @@ size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
   return (size_t)B * Hq * num_splits * ((size_t)d + 1) * sizeof(float);
 }
 
+int decode_resident_per_cu(int d) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (d) {
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<64, DecTile<64, 64, 3>>, 64, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<128, DecTile<128, 64, 2>>, 64, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<256, DecTile<256, 32, 2>>, 64, 0); break;
+    default: break;
+  }
+  if (e != hipSuccess) (void)hipGetLastError();  // leave no sticky error behind
+  return e == hipSuccess && n > 0 ? n : 2;
+}
+
 bool decode_supported(int d, int group) {
   return (d == 64 || d == 128 || d == 256) && group >= 1 && group <= kMaxGroup;
 }

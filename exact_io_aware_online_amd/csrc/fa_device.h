@@ -181,6 +181,20 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Quiet NaN (bf16 0x7FC0, two per word) over rows [r0, r1) of a bf16 array
+// whose row r holds ROWB bytes at base + r * stride; the threads of a
+// workgroup share the 16-byte pieces. Packed batches use it to mark every
+// output row of a sequence that is longer than the launch covers.
+template <int ROWB>
+__device__ __forceinline__ void fill_nan_rows(char* base, int64_t stride, int r0, int r1, int tid, int nthreads) {
+  constexpr int CPR = ROWB / 16;
+  const u32x4 nan4 = {0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+  for (int64_t i = tid; i < (int64_t)(r1 - r0) * CPR; i += nthreads) {
+    const int r = r0 + (int)(i / CPR), c = (int)(i % CPR);
+    *reinterpret_cast<u32x4*>(base + r * stride + c * 16) = nan4;
+  }
+}
+
 __device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS3 i16x4*)(uintptr_t)lds_addr);
 }

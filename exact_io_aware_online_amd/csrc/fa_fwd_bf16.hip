@@ -26,10 +26,13 @@
 //
 // Softmax runs in base 2: t = s * scale * log2(e), the running maximum m in
 // the same units, alpha = 2^(m - m') (FlashAttention: Part 2, section 6.2
-// gives alpha = e^(m - m'); e^x = 2^(x log2 e)). When no row maximum of a
-// wavefront moved, alpha is exactly 1 for every row and the rescale of the
-// accumulator is skipped (bit-identical). Normalisation is deferred to the
-// end (FlashAttention: Part 2, section 1.3), where the row's log-sum-exp is
+// gives alpha = e^(m - m'); e^x = 2^(x log2 e)). The reference m is moved
+// lazily: only when some row of the wavefront sees a score more than
+// kSlack (8, base 2) above its current reference are m, l and the
+// accumulator rescaled; otherwise probabilities 2^(t - m) stay below 2^8
+// and both the accumulator and l keep the old reference, which leaves
+// O = acc / l unchanged. Normalisation is deferred to the end
+// (FlashAttention: Part 2, section 1.3), where the row's log-sum-exp is
 // written as ln2 * (m + log2 l).
 #include <type_traits>
 
@@ -132,9 +135,21 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   int qrow0, Nqb, krow0, Nkb;
   if (p.cu_q != nullptr) {
     qrow0 = min(max(p.cu_q[b], 0), p.total_q);
-    Nqb = min(min(max(p.cu_q[b + 1], qrow0), p.total_q) - qrow0, p.Nq);
+    const int lq = min(max(p.cu_q[b + 1], qrow0), p.total_q) - qrow0;
     krow0 = min(max(p.cu_k[b], 0), p.total_k);
     Nkb = min(max(p.cu_k[b + 1], krow0), p.total_k) - krow0;
+    if (lq > p.Nq) {
+      // longer than the grid's max_seqlen_q: every O and LSE row of the
+      // sequence becomes NaN (the last query tile's workgroup also covers
+      // the rows past the grid) rather than a partial result
+      const int r1 = qt == p.n_qtiles - 1 ? lq : min(q0 + C::BM, lq);
+      fill_nan_rows<D * 2>(p.o + (int64_t)qrow0 * p.Hq * D * 2 + (int64_t)hq * D * 2, (int64_t)p.Hq * D * 2, q0, r1,
+                           tid, C::THREADS);
+      if (p.lse != nullptr)
+        for (int r = q0 + tid; r < r1; r += C::THREADS) p.lse[(int64_t)hq * p.total_q + qrow0 + r] = __builtin_nanf("");
+      return;
+    }
+    Nqb = lq;
   } else {
     qrow0 = b * p.Nq;
     Nqb = p.Nq;

@@ -124,13 +124,15 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
  * num_splits <= 1); 0 also for invalid sizes. */
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
 
-/* A num_splits for B sequences of at most `capacity` keys and Hkv key/value
- * heads on a device with `num_cus` compute units, each holding `wgs_per_cu`
- * resident decode wavefronts (pass 0 for either to use the current
- * device's count and 3 per CU): splits of about 1024 keys, at least enough
- * splits to fill every resident slot, and no more than 64 split workgroups
- * per resident slot. Always >= 1. */
-int fa_kvcache_default_splits(int B, int Hkv, int capacity, int num_cus, int wgs_per_cu);
+/* A num_splits for fa_fwd_kvcache on B sequences of at most `capacity`
+ * keys, Hkv key/value heads and head dimension d, on a device with
+ * `num_cus` compute units each holding `wgs_per_cu` resident decode
+ * workgroups. Pass 0 for num_cus to use the current device's count, and 0
+ * for wgs_per_cu to take it from hipOccupancyMaxActiveBlocksPerMultiprocessor
+ * for the decode kernel that d selects (2 if no device can be queried).
+ * Splits of about 1024 keys, at least enough splits to fill every resident
+ * slot, and no more than 64 split workgroups per resident slot. Always >= 1. */
+int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu);
 
 /* fa_fwd with a local window, aligned to the bottom-right corner
  * (pyshine.com FlashAttention code tour: bottom-right causal alignment

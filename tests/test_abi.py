@@ -34,7 +34,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings_and_version():
-    assert fa.fa_abi_version() == 1
+    assert fa.fa_abi_version() == 2
     for s in range(5):
         assert fa.fa_status_string(s).startswith("FA_")
     assert fa.fa_status_string(99) == "FA_ERR_UNKNOWN"
@@ -110,12 +110,12 @@ def test_workspace_size_formula():
 
 
 def test_default_splits():
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 256, 3) == 8      # ~1024-key splits
-    assert fa.fa_kvcache_default_splits(1, 8, 8192, 256, 3) == 96      # fill 768 resident slots
-    assert fa.fa_kvcache_default_splits(1, 1, 64, 256, 3) == 1         # one 64-key block: cannot split
-    assert fa.fa_kvcache_default_splits(4096, 8, 8192, 256, 3) == 1    # capped by the slot budget
-    assert fa.fa_kvcache_default_splits(0, 8, 8192, 256, 3) == 1
-    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 256, 3) == (1000000 + 1023) // 1024
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 8      # ~1024-key splits
+    assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 96      # fill 768 resident slots
+    assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one 64-key block: cannot split
+    assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # capped by the slot budget
+    assert fa.fa_kvcache_default_splits(0, 8, 8192, 128, 256, 3) == 1
+    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 128, 256, 3) == (1000000 + 1023) // 1024
 
 
 def test_paged_decode_host_validation():

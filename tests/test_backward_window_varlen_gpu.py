@@ -136,3 +136,45 @@ def test_backward_varlen_equals_dense_bitwise():
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(pk(x), y)
+
+
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_backward_varlen_sequence_longer_than_max_seqlen_is_nan(which):
+    # a sequence longer than max_seqlen_q (or _k) gets NaN in every dq, dk
+    # and dv row (rows past the grid included); the others are unaffected
+    lq, lk = [150, 200, 70], [150, 260, 90]
+    Hq, Hkv, d = 4, 2, 128
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(118)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = torch.randn(int(cu_q[-1]), Hq, d, generator=g).to(torch.bfloat16).to(dev)
+    k = torch.randn(int(cu_k[-1]), Hkv, d, generator=g).to(torch.bfloat16).to(dev)
+    v = torch.randn(int(cu_k[-1]), Hkv, d, generator=g).to(torch.bfloat16).to(dev)
+    do = torch.randn(int(cu_q[-1]), Hq, d, generator=g).to(torch.bfloat16).to(dev)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    cq, ck = torch.tensor(cu_q, device=dev), torch.tensor(cu_k, device=dev)
+    m = fa()
+    o, lse = m.fa_fwd_varlen(q, k, v, cq, ck, max(lq), -1, 0, scale=scale)
+    mq, mk = (150, max(lk)) if which == "q" else (max(lq), 200)
+    dq, dk, dv = (torch.zeros_like(t) for t in (q, k, v))
+    m.fa_bwd_varlen(q, k, v, o, lse, do, cq, ck, mq, mk, -1, 0, scale=scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    bq, bk = slice(int(cu_q[1]), int(cu_q[2])), slice(int(cu_k[1]), int(cu_k[2]))
+    assert torch.isnan(dq[bq].float()).all()
+    assert torch.isnan(dk[bk].float()).all() and torch.isnan(dv[bk].float()).all()
+    rq, rk, rv = O.attention_backward_varlen(f64(q), f64(k), f64(v), f64(do), cu_q, cu_k, -1, 0, scale)
+    for sq_, sk_ in ((slice(0, int(cu_q[1])), slice(0, int(cu_k[1]))),
+                     (slice(int(cu_q[2]), int(cu_q[3])), slice(int(cu_k[2]), int(cu_k[3])))):
+        check("dq", dq[sq_], rq[sq_])
+        check("dk", dk[sk_], rk[sk_])
+        check("dv", dv[sk_], rv[sk_])
+
+
+def test_backward_split_pass_variant_takes_windows_and_packed_batches(monkeypatch):
+    # FA_BWD_VARIANT=1 computes dK and dV in two passes; it must honour the
+    # window rule and the packed layout like the default kernel
+    monkeypatch.setenv("FA_BWD_VARIANT", "1")
+    test_backward_window(WINDOW_CASES[2])
+    test_backward_window(WINDOW_CASES[3])
+    test_backward_varlen(VARLEN_CASES[1])

@@ -26,6 +26,93 @@ def fa():
     return m
 
 
+# e4m3 magnitudes in increasing order, from the format definition
+_E4M3 = F8.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8))
+# Score error allowed for the kernel's float32 arithmetic, in the base-2
+# exponent t = scale log2(e) S: exact e4m3 products summed in float32,
+# one float32 multiply, and v_exp_f32 (about 2^-22 relative of x) are all
+# well inside it.
+_DT = 2.0 ** -14
+
+
+def _flip_vectors(t_row, v_rows, den, M):
+    """For the probabilities of one row whose unrounded value x =
+    2^(t - M + 6) lies within the float32 uncertainty of an e4m3 rounding
+    midpoint: the change in that row's O if x took the other neighbouring
+    code. Returns a list of (d,) vectors."""
+    x = 2.0 ** (t_row - M + F8.P_BIAS)
+    hi = np.clip(np.searchsorted(_E4M3, x, side="left"), 1, len(_E4M3) - 1)
+    lo = hi - 1
+    mid = (_E4M3[lo] + _E4M3[hi]) / 2
+    near = np.abs(x - mid) <= _DT * math.log(2.0) * x + 1e-12
+    out = []
+    code = F8.e4m3_decode(F8.e4m3_encode(x))
+    for j in np.nonzero(near)[0]:
+        other = _E4M3[hi[j]] if code[j] == _E4M3[lo[j]] else _E4M3[lo[j]]
+        out.append((other - code[j]) * 2.0 ** -F8.P_BIAS * v_rows[j] / den)
+    return out
+
+
+def assert_fp8_matches(o, lse, ins, Nq, Nk, causal, scale, rows_of=None):
+    """O within the absolute bf16 bar (2e-2) and LSE within 1e-3 of the FP8
+    oracle on the same codes. A row may exceed the O bar only when the
+    oracle shows why: some of its probabilities sit within float32 rounding
+    of an e4m3 midpoint (the kernel computes scores in float32, the oracle in
+    float64), and rounding those the other way brings the row within the
+    bar. `rows_of` restricts the check to given (b, h) slices."""
+    q8, qs, k8, ks, vt8, vs = (t.numpy() if hasattr(t, "numpy") else t for t in ins)
+    qe, ke, ve = (x.astype(np.int64) - 127 for x in (qs, ks, vs))
+    v_rows = np.swapaxes(vt8, 2, 3)
+    Hq, Hkv = q8.shape[1], k8.shape[1]
+    G = Hq // Hkv
+    c = scale * math.log2(math.e)
+    O = f64(o)
+    L = f64(lse)
+    pairs = rows_of or [(b, h) for b in range(q8.shape[0]) for h in range(Hq)]
+    worst = worst_l = 0.0
+    excused = 0
+    for b, h in pairs:
+        kv = h // G
+        sl = lambda t, hh: t[b:b + 1, hh:hh + 1]
+        o_ref, l_ref = F8.attention_fp8(sl(q8, h), sl(qe, h), sl(k8, kv), sl(ke, kv), sl(v_rows, kv), sl(ve, kv),
+                                        Nq, Nk, causal, scale)
+        Lg = L[b, h]
+        fin = np.isfinite(l_ref[0, 0])
+        assert np.array_equal(np.isfinite(Lg), fin)
+        worst_l = max(worst_l, float(np.max(np.abs(Lg[fin] - l_ref[0, 0][fin]), initial=0.0)))
+        err = np.abs(O[b, :, h] - o_ref[0, :, 0])
+        worst = max(worst, float(np.max(err, initial=0.0)))
+        bad = np.nonzero(np.max(err, axis=1) > TOL_O)[0] if Nq else []
+        if len(bad):
+            Qd = F8.dequantize_bhnd(sl(q8, h), sl(qe, h))[0, 0]
+            Kd = F8.dequantize_bhnd(sl(k8, kv), sl(ke, kv))[0, 0, :Nk]
+            Vd = F8.dequantize_bhnd(sl(v_rows, kv), sl(ve, kv))[0, 0, :Nk]
+        for i in bad:
+            vis = np.arange(Nk) <= i if causal else np.ones(Nk, dtype=bool)
+            t = c * (Kd[vis] @ Qd[i])
+            M = math.ceil(float(np.max(t)))
+            den = float(np.sum(2.0 ** (t - M)))
+            flips = _flip_vectors(t, Vd[vis], den, M)
+            # greedy: apply the midpoint flip that most reduces the row's error
+            r = O[b, i, h] - o_ref[0, i, 0]
+            used = set()
+            while np.max(np.abs(r)) > TOL_O:
+                best = min((n for n in range(len(flips)) if n not in used),
+                           key=lambda n: np.max(np.abs(r - flips[n])), default=None)
+                if best is None or np.max(np.abs(r - flips[best])) >= np.max(np.abs(r)):
+                    break
+                used.add(best)
+                r = r - flips[best]
+            assert np.max(np.abs(r)) <= TOL_O, (
+                f"row b={b} i={i} h={h}: max|dO| {np.max(err[i]):.3e} not explained by "
+                f"{len(flips)} near-midpoint probabilities")
+            excused += 1
+    note(f"  max|dO|={worst:.3e} max|dLSE|={worst_l:.3e}; {excused} rows over the O bar, each explained by "
+         f"near-midpoint probability codes")
+    assert worst_l <= TOL_LSE
+    return excused
+
+
 def f64(t):
     return t.detach().to("cpu", torch.float64).numpy()
 
@@ -119,21 +206,8 @@ def test_fwd_fp8_matches_oracle(case):
     scale = float(np.float32(1.0 / math.sqrt(d)))
     o, lse = fa().fa_fwd_fp8(*(t.to(dev) for t in ins), Nq, Nk, causal=causal, scale=scale)
     torch.cuda.synchronize()
-    o_ref, l_ref = F8.attention_fp8(q8.numpy(), qs.numpy().astype(np.int64) - 127, k8.numpy(),
-                                    ks.numpy().astype(np.int64) - 127, np.swapaxes(vt8.numpy(), 2, 3),
-                                    vs.numpy().astype(np.int64) - 127, Nq, Nk, causal, scale)
-    eo = float(np.max(np.abs(f64(o) - o_ref)))
-    L = f64(lse)
-    fin = np.isfinite(l_ref)
-    assert np.array_equal(np.isfinite(L), fin)
-    el = float(np.max(np.abs(L[fin] - l_ref[fin]), initial=0.0))
-    # The bf16 bar scaled by the output's size (as the backward tests do): a
-    # probability within float32 rounding of an e4m3 midpoint may take the
-    # other code (kernel scores are float32, the oracle's float64), moving a
-    # row that averages few values by a few percent of one value.
-    tol = TOL_O * max(1.0, float(np.max(np.abs(o_ref))))
-    note(f"  max|dO|={eo:.3e} (max|O|={np.max(np.abs(o_ref)):.2f}, bound {tol:.3e}) max|dLSE|={el:.3e}")
-    assert eo <= tol and el <= TOL_LSE
+    excused = assert_fp8_matches(o, lse, ins, Nq, Nk, causal, scale)
+    assert excused <= max(2, Nq * B * Hq // 1000)
 
 
 def test_fwd_fp8_no_keys():
@@ -167,9 +241,22 @@ def test_fp8_pipeline_error_against_exact_attention(d):
         signs = SI.random_signs(d, seed=341).to(dev) if rot else None
         o, _ = _pipeline(q, k, v, True, signs)
         torch.cuda.synchronize()
-        rel = float(np.sqrt(np.mean((f64(o) - ref) ** 2) / np.mean(ref ** 2)))
-        note(f"  d={d} rotation={rot}: relative RMS error {rel:.4f}")
+        err = np.abs(f64(o) - ref)
+        rel = float(np.sqrt(np.mean(err ** 2) / np.mean(ref ** 2)))
+        # Element-wise: each output is a convex combination of the visible
+        # values, and FP8 moves it by rounding every value (at most 2^-4
+        # relative) and every weight (the weights' 2^-4 rounding plus the
+        # shift that rounded scores cause); the error of an element stays a
+        # fraction of the largest visible |v| in its column. The bound is
+        # 2^-2 of it (the oracle's FP8 pipeline on such inputs reaches about
+        # 0.11 of it, at the first causal rows, which average few values).
+        vmax = np.maximum.accumulate(np.abs(f64(v)[0]), axis=0)        # (N, Hkv, d): max over keys 0..i
+        bound = 2.0 ** -2 * np.repeat(vmax, q.shape[2] // k.shape[2], axis=1)[None]
+        frac = float(np.max(err / bound))
+        note(f"  d={d} rotation={rot}: relative RMS error {rel:.4f}, max|dO| {err.max():.3e}, "
+             f"max |dO| / (2^-2 max|v|) {frac:.3f}")
         assert rel < 0.08
+        assert frac <= 1.0
 
 
 def test_rotation_reduces_error_with_outlier_features():
@@ -206,12 +293,5 @@ def test_fp8_full_size_sampled():
     scale = float(np.float32(1.0 / math.sqrt(d)))
     o, lse = fa().fa_fwd_fp8(*(t.to(dev) for t in ins), N, N, causal=True, scale=scale)
     torch.cuda.synchronize()
-    q8, qs, k8, ks, vt8, vs = (t.numpy() for t in ins)
-    for b, h in ((0, 0), (B - 1, H - 1), (3, 7)):
-        sl = lambda t: t[b:b + 1, h:h + 1]
-        o_ref, l_ref = F8.attention_fp8(sl(q8), sl(qs).astype(np.int64) - 127, sl(k8), sl(ks).astype(np.int64) - 127,
-                                        np.swapaxes(sl(vt8), 2, 3), sl(vs).astype(np.int64) - 127, N, N, True, scale)
-        eo = float(np.max(np.abs(f64(o[b:b + 1, :, h:h + 1]) - o_ref)))
-        el = float(np.max(np.abs(f64(lse[b:b + 1, h:h + 1]) - l_ref)))
-        note(f"  b={b} h={h}: max|dO|={eo:.3e} max|dLSE|={el:.3e}")
-        assert eo <= TOL_O and el <= TOL_LSE
+    excused = assert_fp8_matches(o, lse, ins, N, N, True, scale, rows_of=[(0, 0), (B - 1, H - 1), (3, 7)])
+    assert excused <= 3

@@ -263,7 +263,7 @@ def test_decode_full_size_sampled(name):
     q, kc, vc, lens = SI.decode_inputs(device=dev, **w)
     scale = f32scale(w["d"])
     m = fa()
-    S = m.fa_kvcache_default_splits(w["B"], w["Hkv"], w["capacity"])
+    S = m.fa_kvcache_default_splits(w["B"], w["Hkv"], w["capacity"], w["d"])
     o, lse = m.fa_fwd_kvcache(q, kc, vc, lens, num_splits=S, scale=scale)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()

@@ -120,3 +120,30 @@ def test_varlen_equals_dense_per_sequence_bitwise():
     torch.cuda.synchronize()
     assert torch.equal(od.reshape(600, 4, 128), ov)
     assert torch.equal(ld.permute(1, 0, 2).reshape(4, 600), lv)
+
+
+def test_varlen_sequence_longer_than_max_seqlen_is_nan():
+    # max_seqlen_q sizes the launch; a sequence longer than it gets NaN in
+    # every O and LSE row (the rows past the grid included), and the other
+    # sequences are unaffected
+    lq, lk = [150, 300, 70], [150, 320, 90]
+    Hq, Hkv, d = 4, 2, 128
+    dev = torch.device("cuda")
+    g = torch.Generator().manual_seed(95)
+    cu_q = np.concatenate([[0], np.cumsum(lq)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lk)]).astype(np.int32)
+    q = torch.randn(int(cu_q[-1]), Hq, d, generator=g).to(torch.bfloat16)
+    k = torch.randn(int(cu_k[-1]), Hkv, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(int(cu_k[-1]), Hkv, d, generator=g).to(torch.bfloat16)
+    scale = float(np.float32(1.0 / math.sqrt(d)))
+    o = torch.zeros(int(cu_q[-1]), Hq, d, dtype=torch.bfloat16, device=dev)
+    lse = torch.zeros(Hq, int(cu_q[-1]), dtype=torch.float32, device=dev)
+    fa().fa_fwd_varlen(q.to(dev), k.to(dev), v.to(dev), torch.tensor(cu_q, device=dev), torch.tensor(cu_k, device=dev),
+                       200, -1, 0, o=o, lse=lse, scale=scale)
+    torch.cuda.synchronize()
+    bad = slice(int(cu_q[1]), int(cu_q[2]))
+    assert torch.isnan(o[bad].float()).all() and torch.isnan(lse[:, bad]).all()
+    o_ref, l_ref = O.attention_varlen(f64(q), f64(k), f64(v), cu_q, cu_k, -1, 0, scale)
+    for s in (slice(0, int(cu_q[1])), slice(int(cu_q[2]), int(cu_q[3]))):
+        assert np.max(np.abs(f64(o[s]) - o_ref[s])) <= 2e-2
+        assert np.max(np.abs(f64(lse[:, s]) - l_ref[:, s])) <= 1e-3
