@@ -23,6 +23,8 @@ __all__ = [
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
     "fa_fwd_kvcache_paged",
+    "fa_fwd_kvcache_noalloc",
+    "FA_NOALLOC_SCRATCH_BYTES",
     "fa_fwd_kvcache_append",
     "fa_fwd_kvcache_paged_append",
     "fa_fp8_padded_rows",
@@ -38,6 +40,7 @@ __all__ = [
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_LAUNCH = range(5)
 FA_DTYPE_BF16, FA_DTYPE_F32 = 0, 1
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # the static per-GPU scratch of fa_fwd_kvcache_noalloc
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
@@ -72,6 +75,8 @@ def lib():
     L.fa_fwd_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, i, f, vp]
     L.fa_fwd_kvcache.restype = i
     L.fa_fwd_kvcache.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    L.fa_fwd_kvcache_noalloc.restype = i
+    L.fa_fwd_kvcache_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     L.fa_fwd_kvcache_workspace_size.restype = sz
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
     L.fa_kvcache_default_splits.restype = i
@@ -314,6 +319,47 @@ def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_split
                               _stream(stream))
     if st != FA_OK:
         raise FAError(st, "fa_fwd_kvcache")
+    return o, lse
+
+
+def fa_fwd_kvcache_noalloc(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_splits=None, scale=None,
+                           stream=None, want_lse=True):
+    """Split-KV decode through ``fa_fwd_kvcache_noalloc``: as
+    ``fa_fwd_kvcache``, but the library keeps the split partials in its own
+    static per-GPU scratch (FA_NOALLOC_SCRATCH_BYTES), so the call itself
+    allocates nothing on the device. Calls that overlap on one GPU race on
+    that scratch. ``o`` and ``lse`` are allocated here when not given.
+    """
+    import torch
+    if q.dim() != 4 or q.shape[1] != 1:
+        raise ValueError("q must be (batch, 1, heads, head_dim)")
+    B, _, Hq, d = q.shape
+    if kcache.dim() != 4:
+        raise ValueError("kcache must be (batch, capacity, heads, head_dim)")
+    _, cap, Hkv, dk = kcache.shape
+    if dk != d or tuple(vcache.shape) != tuple(kcache.shape) or kcache.shape[0] != B:
+        raise ValueError("cache shapes do not match q")
+    for t, n in ((q, "q"), (kcache, "kcache"), (vcache, "vcache")):
+        _check(t, n, torch.bfloat16, q.device)
+    _check(cache_seqlens, "cache_seqlens", torch.int32, q.device)
+    _shape(cache_seqlens, (B,), "cache_seqlens")
+    if num_splits is None:
+        num_splits = fa_kvcache_default_splits(B, Hkv, cap, d)
+    if o is None:
+        o = torch.empty_like(q)
+    _check(o, "o", torch.bfloat16, q.device)
+    _shape(o, q.shape, "o")
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check(lse, "lse", torch.float32, q.device)
+        _shape(lse, (B, Hq), "lse")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    st = lib().fa_fwd_kvcache_noalloc(_ptr(q), _ptr(kcache), _ptr(vcache), _ptr(cache_seqlens), _ptr(o), _ptr(lse),
+                                      int(num_splits), B, Hq, Hkv, cap, d, float(scale), _stream(stream))
+    if st != FA_OK:
+        raise FAError(st, "fa_fwd_kvcache_noalloc")
     return o, lse
 
 

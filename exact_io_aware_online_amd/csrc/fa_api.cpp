@@ -9,11 +9,40 @@
 
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
 
 namespace {
+
+// Scratch of the allocation-free decode entry point: one copy per GPU in
+// static device memory, resolved to a device address once per device.
+__device__ __align__(256) unsigned char scratch[FA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's `scratch` (looked up with that
+// device current on its first use), or null if the lookup fails. Host code
+// uses only this address: the array's own name is a host-side stand-in.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr int kAbiVersion = 2;
 
@@ -185,7 +214,8 @@ fa_status_t kvcache(const void* q, const void* k_new, const void* v_new, const v
                     const int32_t* block_table, int page_size, int pages_per_seq, int num_pages,
                     const int32_t* cache_seqlens, void* o, float* lse, int causal,
                     int num_splits, int B, int Nq, int Hq, int Hkv, int capacity, int d,
-                    float scale, void* workspace, size_t workspace_bytes, void* stream) {
+                    float scale, void* workspace, size_t workspace_bytes, void* stream,
+                    bool check_only = false) {
   if (B < 0 || Nq < 1 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
@@ -196,6 +226,7 @@ fa_status_t kvcache(const void* q, const void* k_new, const void* v_new, const v
   if (B == 0) return FA_OK;
   if (q == nullptr || o == nullptr || cache_seqlens == nullptr) return FA_ERR_INVALID_ARG;
   if (capacity > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_INVALID_ARG;
+  if (check_only) return FA_OK;  // every check but the workspace's
   const size_t need = fa::decode_workspace_bytes(B * Nq, Hq, d, num_splits);
   if (need > 0 && (workspace == nullptr || workspace_bytes < need)) return FA_ERR_WORKSPACE;
 
@@ -233,6 +264,26 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
   return kvcache(q, nullptr, nullptr, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, 0, num_splits, B, 1,
                  Hq, Hkv, capacity, d, scale, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_fwd_kvcache_noalloc(const void* q, const void* kcache, const void* vcache,
+                                   const int32_t* cache_seqlens, void* o, float* lse,
+                                   int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                                   float scale, void* stream) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || capacity < 0 || d <= 0 || num_splits < 1) return FA_ERR_INVALID_ARG;
+  const size_t need = B > 0 ? fa::decode_workspace_bytes(B, Hq, d, num_splits) : 0;
+  if (need > FA_NOALLOC_SCRATCH_BYTES) return FA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0) {
+    // the argument checks come first: a call they reject must not touch the device
+    const fa_status_t st = kvcache(q, nullptr, nullptr, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, 0,
+                                   num_splits, B, 1, Hq, Hkv, capacity, d, scale, nullptr, 0, nullptr, true);
+    if (st != FA_OK) return st;
+    ws = scratch_on_current_device();
+    if (ws == nullptr) return FA_ERR_LAUNCH;
+  }
+  return kvcache(q, nullptr, nullptr, kcache, vcache, nullptr, 0, 0, 0, cache_seqlens, o, lse, 0, num_splits, B, 1,
+                 Hq, Hkv, capacity, d, scale, ws, need, stream);
 }
 
 fa_status_t fa_fwd_kvcache_append(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,

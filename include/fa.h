@@ -120,6 +120,31 @@ fa_status_t fa_fwd_kvcache(const void* q, const void* kcache, const void* vcache
                            int num_splits, int B, int Hq, int Hkv, int capacity, int d,
                            float scale, void* workspace, size_t workspace_bytes, void* stream);
 
+/* fa_fwd_kvcache for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc. Same arguments, results and errors as fa_fwd_kvcache (the
+ * same kernels run), except that there is no workspace argument: the split
+ * partials go to a scratch array that the library holds in static device
+ * memory, FA_NOALLOC_SCRATCH_BYTES per GPU, for as long as the process
+ * lives. Nothing is allocated or freed by the call.
+ *  - Sizes whose workspace (fa_fwd_kvcache_workspace_size(B, Hq, d,
+ *    num_splits)) exceeds FA_NOALLOC_SCRATCH_BYTES return FA_ERR_WORKSPACE
+ *    before anything is enqueued (fewer splits, or fa_fwd_kvcache with a
+ *    caller workspace, serve larger batches).
+ *  - Every call on one GPU uses that GPU's single scratch array, whose
+ *    contents carry over from the previous call (the kernels write every
+ *    partial before reading it, so nothing has to start cleared). Calls
+ *    that can overlap on one GPU (different streams, or several host
+ *    threads) race on it: order them on one stream.
+ *  - The scratch array of a device is looked up (hipGetSymbolAddress) on the
+ *    first call that needs it with that device current; a failed lookup
+ *    returns FA_ERR_LAUNCH. */
+#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+fa_status_t fa_fwd_kvcache_noalloc(const void* q, const void* kcache, const void* vcache,
+                                   const int32_t* cache_seqlens, void* o, float* lse,
+                                   int num_splits, int B, int Hq, int Hkv, int capacity, int d,
+                                   float scale, void* stream);
+
 /* Bytes of workspace fa_fwd_kvcache needs for these sizes (0 when
  * num_splits <= 1); 0 also for invalid sizes. */
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);

@@ -226,3 +226,28 @@ def test_backward_window_varlen_host_validation():
     assert var(cu=null) == fa.FA_ERR_INVALID_ARG
     assert var() == fa.FA_ERR_WORKSPACE
     assert var(B=0, cu=null) == fa.FA_OK
+
+
+def test_noalloc_decode_host_validation():
+    L = fa.lib()
+    null = None
+    f = ctypes.c_float(0.1)
+    # the Python constant is the header's
+    text = open(HEADER).read()
+    assert "#define FA_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+    assert fa.FA_NOALLOC_SCRATCH_BYTES == 16 << 20
+    # beyond the static scratch: rejected before anything else
+    assert L.fa_fwd_kvcache_noalloc(null, null, null, null, null, null, 8, 4096, 32, 8, 8192, 128, f,
+                                    null) == fa.FA_ERR_WORKSPACE
+    # within it, but bad arguments: rejected on the host, no device lookup
+    assert L.fa_fwd_kvcache_noalloc(null, null, null, null, null, null, 4, 8, 8, 2, 256, 128, f,
+                                    null) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_kvcache_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, null, 0, 8, 8, 2, 256, 128, f,
+                                    null) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_kvcache_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, null, 4, 8, 6, 4, 256, 128, f,
+                                    null) == fa.FA_ERR_INVALID_ARG
+    assert L.fa_fwd_kvcache_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, null, 4, 8, 8, 2, 256, 96, f,
+                                    null) == fa.FA_ERR_UNSUPPORTED
+    # B = 0 is a no-op
+    assert L.fa_fwd_kvcache_noalloc(null, null, null, null, null, null, 4, 0, 8, 2, 256, 128, f,
+                                    null) == fa.FA_OK
