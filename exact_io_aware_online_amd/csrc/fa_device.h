@@ -181,6 +181,36 @@ __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
 }
 
+// An empty statement that reads its operands: every instruction that
+// produces them stays ahead of this point in the program (the compiler may
+// not sink their computation past it, e.g. into a later block).
+__device__ __forceinline__ void materialize(const bf16x8& x) {
+  asm volatile("" ::"v"(__builtin_bit_cast(u32x4, x)));
+}
+__device__ __forceinline__ void materialize(float x) { asm volatile("" ::"v"(x)); }
+
+// x *= s for an accumulator tile held in accumulation registers (AGPRs),
+// done in place with read / multiply / write per element. Written as one
+// asm statement so that the compiler sees no vector-ALU use of the tile:
+// it keeps the tile in AGPRs instead of moving it to VGPRs around a
+// rarely taken rescale.
+__device__ __forceinline__ void scale_agpr16(f32x16& x, float s) {
+  float e0 = x[0], e1 = x[1], e2 = x[2], e3 = x[3], e4 = x[4], e5 = x[5], e6 = x[6], e7 = x[7];
+  float e8 = x[8], e9 = x[9], e10 = x[10], e11 = x[11], e12 = x[12], e13 = x[13], e14 = x[14], e15 = x[15];
+  float t;
+#define FA_SCALE_ONE(i) \
+  "v_accvgpr_read_b32 %[t], %[e" #i "]\n\tv_mul_f32 %[t], %[t], %[s]\n\tv_accvgpr_write_b32 %[e" #i "], %[t]\n\t"
+  asm volatile(FA_SCALE_ONE(0) FA_SCALE_ONE(1) FA_SCALE_ONE(2) FA_SCALE_ONE(3) FA_SCALE_ONE(4) FA_SCALE_ONE(5)
+               FA_SCALE_ONE(6) FA_SCALE_ONE(7) FA_SCALE_ONE(8) FA_SCALE_ONE(9) FA_SCALE_ONE(10) FA_SCALE_ONE(11)
+               FA_SCALE_ONE(12) FA_SCALE_ONE(13) FA_SCALE_ONE(14) FA_SCALE_ONE(15)
+               : [t] "=&v"(t), [e0] "+a"(e0), [e1] "+a"(e1), [e2] "+a"(e2), [e3] "+a"(e3), [e4] "+a"(e4),
+                 [e5] "+a"(e5), [e6] "+a"(e6), [e7] "+a"(e7), [e8] "+a"(e8), [e9] "+a"(e9), [e10] "+a"(e10),
+                 [e11] "+a"(e11), [e12] "+a"(e12), [e13] "+a"(e13), [e14] "+a"(e14), [e15] "+a"(e15)
+               : [s] "v"(s));
+#undef FA_SCALE_ONE
+  x = f32x16{e0, e1, e2, e3, e4, e5, e6, e7, e8, e9, e10, e11, e12, e13, e14, e15};
+}
+
 // Quiet NaN (bf16 0x7FC0, two per word) over rows [r0, r1) of a bf16 array
 // whose row r holds ROWB bytes at base + r * stride; the threads of a
 // workgroup share the 16-byte pieces. Packed batches use it to mark every

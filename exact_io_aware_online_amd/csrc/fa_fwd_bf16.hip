@@ -66,10 +66,13 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_>
+template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_, bool PIPE_ = false>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_, QB = QB_, NST = NST_;
   static constexpr int WAVES_PER_SIMD = WPS_;  // register budget: 512 / WPS per lane
+  // one wavefront per SIMD, two query blocks per wavefront, each tile's
+  // MFMA phases overlapped with the other block's softmax (see the kernel)
+  static constexpr bool PIPE = PIPE_;
   // ring stage as an immediate LDS offset (one copy of the tile code per
   // stage); head dimension 256 has no registers to spare for it
   static constexpr bool CONST_STAGE = D_ < 256;
@@ -525,6 +528,221 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       u_hi = min(max((fhi + 1) / BN - t0, u_lo), t_hi);
     }
   }
+  if constexpr (C::PIPE) {
+    // Software pipeline of one wavefront per SIMD over two 32-row query
+    // blocks A and B (64 rows), 32-key tiles. Every K and V^T operand is
+    // read from LDS once per tile, held in registers, and feeds two MFMAs,
+    // one per block: half the LDS bytes per flop of the one-block shape.
+    // With no second wavefront on the SIMD to fill the matrix pipe during a
+    // softmax, the wavefront overlaps its own, skewed by half a tile so
+    // that every MFMA phase has softmax work beside it:
+    //   P1: S_A(t) = K Q_A^T        | softmax(B, t-1) second half
+    //   P2: O_B += V^T P_B^T (t-1)  | softmax(A, t) first half
+    //   P3: S_B(t) = K Q_B^T        | softmax(A, t) second half; V^T(t) operands read
+    //   (wait + barrier for tile t+1, its loads issued)
+    //   P4: O_A += V^T P_A^T (t)    | softmax(B, t) first half; K(t+1) operands read
+    // (FlashAttention: Part 2, section 1.5: overlap the softmax of one part
+    // of the work with the matrix products of another.) Inside a phase each
+    // MFMA is followed by one step of the softmax, with scheduling fences
+    // between them, so the issue order is exactly that: the matrix pipe
+    // runs the MFMA while the vector ALU runs the step.
+    static_assert(QB == 2 && BN == 32 && NBT == 1, "pipelined shape");
+    constexpr int NK = D / 16;           // K operands (and S MFMAs) per tile and block
+    constexpr int NDT = D / 32;          // V^T blocks: PV MFMAs per tile and block = 2 NDT
+    static_assert(NK == 8 && NDT == 4, "the step schedule below assumes d = 128");
+    bf16x8 kf[NK];
+    i16x4 vr[NDT][2][2];
+    float mu[2];       // reference of the block's probabilities of its current tile
+    float alpha[2];    // its rescale factor, applied to the accumulator before its PV
+    bool rs[2];        // whether the reference moved (wave-uniform)
+    float mx[2];
+
+    auto fence = [] __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+    auto stage_of = [&](int t) __attribute__((always_inline)) {
+      return (uint32_t)__builtin_amdgcn_readfirstlane((t % NST) * C::TILE_BYTES);
+    };
+    auto kread = [&](uint32_t stg, int i) __attribute__((always_inline)) {
+      kf[i] = *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + k_off[i]);
+    };
+    auto vread = [&](uint32_t stg, int i) __attribute__((always_inline)) {  // i = 0 .. 15
+      const int dt = i >> 2, kk = (i >> 1) & 1, h = i & 1;
+      vr[dt][kk][h] = ds_read_tr(lds0 + stg + v_off[dt][h] + kk * 16 * D * 2);
+    };
+    auto mfma_s = [&](int qb, int i) __attribute__((always_inline)) {
+      sc[qb][0] = mfma32x32x16(kf[i], qf[qb][i], i == 0 ? f32x16{} : sc[qb][0]);
+    };
+    auto mfma_pv = [&](int qb, int i) __attribute__((always_inline)) {
+      const int dt = i >> 1, kk = i & 1;
+      const i16x4 v0 = vr[dt][kk][0], v1 = vr[dt][kk][1];
+      const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[qb][dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, vv), pf[qb][kk], acc[qb][dt]);
+    };
+    auto expv = [&](int qb, int i) __attribute__((always_inline)) {
+      sc[qb][0][i] = exp2_fast(fmaf(sc[qb][0][i], p.c, -mu[qb]));
+      materialize(sc[qb][0][i]);
+    };
+    // First half of block qb's online softmax of tile t, in 8 steps: mask,
+    // row maximum, the (lazy, as in the one-block shape) reference move,
+    // and the first 10 of the 16 probabilities of this lane.
+    auto sm1 = [&](int s, int t, int qb, auto mask_tag) __attribute__((always_inline)) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      if (s <= 1) {
+        if constexpr (MASK) {
+          const int my_q = qw0 + qb * 32 + r32;
+          const int base = (t0 + t) * BN + 4 * g;
+          const int lo = (p.wl >= 0 ? my_q + off - p.wl : 0) - base;
+          const int hi = (p.wr >= 0 ? min(my_q + off + p.wr, Nkb - 1) : Nkb - 1) - base;
+#pragma unroll
+          for (int i = 8 * s; i < 8 * s + 8; ++i) {
+            const int o = 8 * (i >> 2) + (i & 3);
+            if (o < lo || o > hi) sc[qb][0][i] = -INFINITY;
+          }
+        }
+        float x = s == 0 ? fmaxf(sc[qb][0][0], sc[qb][0][1]) : fmaxf(mx[qb], fmaxf(sc[qb][0][8], sc[qb][0][9]));
+#pragma unroll
+        for (int i = 8 * s + 2; i < 8 * s + 8; ++i) x = fmaxf(x, sc[qb][0][i]);
+        mx[qb] = x;
+        materialize(x);
+      } else if (s == 2) {
+        const float m_cand = fmaxf(m[qb], halves_max(mx[qb]) * p.c);
+        rs[qb] = __builtin_amdgcn_ballot_w64(m_cand > m[qb] + kSlack) != 0;  // wave-uniform
+        const float m_new = rs[qb] ? m_cand : m[qb];
+        mu[qb] = (m_new == -INFINITY) ? 0.f : m_new;  // never (-inf) - (-inf)
+        alpha[qb] = rs[qb] ? exp2_fast(m[qb] - mu[qb]) : 1.f;
+        m[qb] = m_new;
+        materialize(mu[qb]);
+        materialize(alpha[qb]);
+      } else if (s == 3) {
+        l[qb] *= alpha[qb];
+        expv(qb, 0);
+        expv(qb, 1);
+        materialize(l[qb]);
+      } else {
+        expv(qb, 2 * s - 6);  // s = 4 .. 7: probabilities 2 .. 9
+        expv(qb, 2 * s - 5);
+      }
+    };
+    // Second half, in 8 steps: the last 6 probabilities, P^T packed to
+    // bf16, and the row sum (after the packing, in place).
+    auto sm2 = [&](int s, int qb) __attribute__((always_inline)) {
+      if (s <= 2) {
+        expv(qb, 10 + 2 * s);
+        expv(qb, 11 + 2 * s);
+      } else if (s <= 4) {
+        const int kk = s - 3;
+        u32x4 w;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) w[e2] = pack_bf16x2(sc[qb][0][8 * kk + 2 * e2], sc[qb][0][8 * kk + 2 * e2 + 1]);
+        pf[qb][kk] = __builtin_bit_cast(bf16x8, w);
+        materialize(pf[qb][kk]);
+      } else if (s == 5) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          sc[qb][0][i] += sc[qb][0][i + 8];
+          materialize(sc[qb][0][i]);
+        }
+      } else if (s == 6) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[qb][0][i] += sc[qb][0][i + 4];
+        sc[qb][0][0] += sc[qb][0][2];
+        sc[qb][0][1] += sc[qb][0][3];
+        materialize(sc[qb][0][0]);
+        materialize(sc[qb][0][1]);
+      } else {
+        l[qb] += sc[qb][0][0] + sc[qb][0][1];
+        materialize(l[qb]);
+      }
+    };
+    auto rescale_acc = [&](int qb) __attribute__((always_inline)) {
+      if (rs[qb]) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) scale_agpr16(acc[qb][dt], alpha[qb]);
+      }
+    };
+
+    // one tile of this wavefront (kf holds K(t); block B's softmax of the
+    // previous tile is half done and its PV pending)
+    auto tile = [&](int t, auto mask_tag) __attribute__((always_inline)) {
+      const uint32_t stg = stage_of(t);
+      // P1
+      static_for<8>([&](auto I) {
+        mfma_s(0, I);
+        fence();
+        sm2(I, 1);
+        fence();
+      });
+      rescale_acc(1);
+      fence();
+      // P2
+      static_for<8>([&](auto I) {
+        mfma_pv(1, I);
+        fence();
+        sm1(I, t, 0, mask_tag);
+        fence();
+      });
+      // P3
+      static_for<8>([&](auto I) {
+        mfma_s(1, I);
+        fence();
+        sm2(I, 0);
+        vread(stg, 2 * I);
+        vread(stg, 2 * I + 1);
+        fence();
+      });
+      rescale_acc(0);
+      // tile t + 1 landed; the stage of tile t - 1 is refilled
+      if (t + 1 < ntiles) sync_tile(t + 1);
+      fence();
+      // P4
+      const uint32_t nstg = stage_of(t + 1);
+      static_for<8>([&](auto I) {
+        mfma_pv(0, I);
+        fence();
+        sm1(I, t, 1, mask_tag);
+        kread(nstg, I);
+        fence();
+      });
+    };
+    // a tile this wavefront does not compute: keep the workgroup's order
+    auto idle = [&](int t) __attribute__((always_inline)) {
+      if (t + 1 < ntiles) sync_tile(t + 1);
+      const uint32_t nstg = stage_of(t + 1);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kread(nstg, i);
+    };
+
+    // Block B starts with a pending tile that contributes nothing: zero
+    // probabilities (the first half already "exponentiated" to 0, the rest
+    // at -inf) and zero V^T operands.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[1][0][i] = i < 10 ? 0.f : -INFINITY;
+    mu[1] = 0.f;
+    alpha[1] = 1.f;
+    rs[1] = false;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) vr[dt][kk][0] = vr[dt][kk][1] = i16x4{};
+
+    // the tiles in order, peeled into runs of one kind (one loop each keeps
+    // the register allocation of every loop free of merged copies)
+    sync_tile(0);
+    {
+      const uint32_t stg0 = stage_of(0);
+#pragma unroll
+      for (int i = 0; i < NK; ++i) kread(stg0, i);
+    }
+    int t = 0;
+    for (; t < t_lo; ++t) idle(t);
+    for (; t < u_lo; ++t) tile(t, std::true_type{});
+    for (; t < u_hi; ++t) tile(t, std::false_type{});
+    for (; t < t_hi; ++t) tile(t, std::true_type{});
+    // drain: block B's last tile
+    static_for<8>([&](auto I) { sm2(I, 1); });
+    rescale_acc(1);
+    static_for<8>([&](auto I) { mfma_pv(1, I); });
+    for (; t < ntiles; ++t) idle(t);
+  } else {
   int t = 0;
   for (; t < t_lo; ++t) sync_tile(t);
   for (; t < u_lo; ++t) {
@@ -553,6 +771,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     compute_any(t, std::true_type{});
   }
   for (; t < ntiles; ++t) sync_tile(t);
+  }
 
   // ---- epilogue: combine the two lane halves' sums, normalise once. At
   // d = 64 and 128 (where the ring has room) the normalised rows go through
@@ -669,13 +888,10 @@ hipError_t launch(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Tile-shape override for tuning (FA_FWD_VARIANT), read once per process.
+// Tile-shape override for tuning (FA_FWD_VARIANT), read at every call.
 int variant() {
-  static const int v = [] {
-    const char* e = getenv("FA_FWD_VARIANT");
-    return e ? atoi(e) : 0;
-  }();
-  return v;
+  const char* e = getenv("FA_FWD_VARIANT");
+  return e ? atoi(e) : 0;
 }
 
 }  // namespace
@@ -696,6 +912,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
       }
     case 128:
       switch (variant()) {
+        case 4: return launch<Cfg<128, 32, 2, 2, 4, 1, true>>(a, stream);
         case 1: return launch<Cfg<128, 64, 8, 1, 2, 2>>(a, stream);
         case 2: return launch<Cfg<128, 32, 8, 1, 2, 2>>(a, stream);
         case 3: return launch<Cfg<128, 64, 8, 1, 3, 2>>(a, stream);

@@ -104,3 +104,27 @@ def test_forward_chunked_order(case):
     o_ref, l_ref = O.attention(f64(q), f64(k), f64(v), True, scale)
     assert np.max(np.abs(f64(o) - o_ref)) <= 2e-2
     assert np.max(np.abs(f64(lse) - l_ref)) <= 1e-3
+
+
+@pytest.mark.parametrize("case", [(2, 4, 2, 300, 300, True), (1, 4, 1, 520, 520, True), (1, 2, 2, 333, 129, False),
+                                  (2, 2, 2, 1, 77, False)], ids=lambda c: "B{}H{}kv{}q{}k{}{}".format(*c))
+def test_pipelined_tile_shape_variant(case, monkeypatch):
+    # FA_FWD_VARIANT=4 selects, at d = 128, the one-wavefront-per-SIMD
+    # pipelined shape (two query blocks per wavefront, 32-key tiles); it
+    # must agree with the oracle like the default shape, and with windows
+    B, Hq, Hkv, Nq, Nk, causal = case
+    monkeypatch.setenv("FA_FWD_VARIANT", "4")
+    dev = torch.device("cuda")
+    q, k, v = SI.prefill_inputs(B=B, Hq=Hq, Hkv=Hkv, Nq=Nq, Nk=Nk, d=128, seed=950 + Nq, device=dev)
+    scale = float(np.float32(1.0 / math.sqrt(128)))
+    import exact_io_aware_online_amd as m
+    o, lse = m.fa_fwd(q, k, v, causal=causal, scale=scale)
+    ow, lw = m.fa_fwd_window(q, k, v, 40, 0, scale=scale)
+    torch.cuda.synchronize()
+    o_ref, l_ref = O.attention(f64(q), f64(k), f64(v), causal, scale)
+    ow_ref, lw_ref = O.attention_window(f64(q), f64(k), f64(v), 40, 0, scale)
+    for got_o, got_l, ro, rl in ((o, lse, o_ref, l_ref), (ow, lw, ow_ref, lw_ref)):
+        fin = np.isfinite(rl)
+        assert np.array_equal(np.isfinite(f64(got_l)), fin)
+        assert np.max(np.abs(f64(got_o) - ro)) <= 2e-2
+        assert np.max(np.abs(f64(got_l)[fin] - rl[fin]), initial=0.0) <= 1e-3
