@@ -436,19 +436,20 @@ def main():
             vn = torch.randn((wd["B"], nq, wd["Hkv"], wd["d"]), generator=g, device=dev).to(torch.bfloat16)
             oa = torch.empty_like(qa)
             la = torch.empty((wd["B"], wd["Hq"], nq), dtype=torch.float32, device=dev)
-            wsa = torch.empty(max(fa.fa_fwd_kvcache_workspace_size(wd["B"] * nq, wd["Hq"], wd["d"], S), 1),
+            Sa = fa.fa_kvcache_append_default_splits(wd["B"], nq, wd["Hkv"], wd["Hq"], wd["capacity"], wd["d"])
+            wsa = torch.empty(max(fa.fa_fwd_kvcache_workspace_size(wd["B"] * nq, wd["Hq"], wd["d"], Sa), 1),
                               dtype=torch.uint8, device=dev)
             rows = int(lens_a.to(torch.int64).sum().item()) + wd["B"] * nq
             a_bytes = (rows * wd["Hkv"] * wd["d"] * 2 * 2 + 2 * kn.numel() * 2 * 2
                        + qa.numel() * 2 + oa.numel() * 2 + la.numel() * 4 + lens.numel() * 4)
 
             def astep():
-                fa.fa_fwd_kvcache_append(qa, kc, vc, lens_a, kn, vn, causal=True, o=oa, lse=la, num_splits=S,
+                fa.fa_fwd_kvcache_append(qa, kc, vc, lens_a, kn, vn, causal=True, o=oa, lse=la, num_splits=Sa,
                                          scale=scale_d, workspace=wsa)
             settle(astep, 0.1, min_calls=3)
             a_ms = timed(astep, args.append_steps)
             a_gbs = a_bytes / (a_ms * 1e-3) / 1e9
-            append[f"q{nq}"] = {"value": round(a_gbs, 1), "unit": "GB/s", "queries_per_seq": nq,
+            append[f"q{nq}"] = {"value": round(a_gbs, 1), "unit": "GB/s", "queries_per_seq": nq, "num_splits": Sa,
                                 "mean_launch_ms": round(a_ms, 5), "frac": round(a_gbs / PEAK_HBM_GBS, 4),
                                 "algorithmic_bytes_per_launch": a_bytes, "steps": args.append_steps}
 

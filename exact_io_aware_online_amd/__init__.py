@@ -22,6 +22,7 @@ __all__ = [
     "fa_fwd_kvcache",
     "fa_fwd_kvcache_workspace_size",
     "fa_kvcache_default_splits",
+    "fa_kvcache_append_default_splits",
     "fa_fwd_kvcache_paged",
     "fa_fwd_kvcache_noalloc",
     "FA_NOALLOC_SCRATCH_BYTES",
@@ -81,6 +82,8 @@ def lib():
     L.fa_fwd_kvcache_workspace_size.argtypes = [i, i, i, i]
     L.fa_kvcache_default_splits.restype = i
     L.fa_kvcache_default_splits.argtypes = [i, i, i, i, i, i]
+    L.fa_kvcache_append_default_splits.restype = i
+    L.fa_kvcache_append_default_splits.argtypes = [i, i, i, i, i, i, i, i]
     L.fa_fwd_kvcache_paged.restype = i
     L.fa_fwd_kvcache_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, f, vp, sz, vp]
     L.fa_fwd_kvcache_append.restype = i
@@ -279,6 +282,11 @@ def fa_kvcache_default_splits(B, Hkv, capacity, d=128, num_cus=0, wgs_per_cu=0):
                                                int(wgs_per_cu)))
 
 
+def fa_kvcache_append_default_splits(B, Nq, Hkv, Hq, capacity, d=128, num_cus=0, wgs_per_cu=0):
+    return int(lib().fa_kvcache_append_default_splits(int(B), int(Nq), int(Hkv), int(Hq), int(capacity), int(d),
+                                                      int(num_cus), int(wgs_per_cu)))
+
+
 def fa_fwd_kvcache(q, kcache, vcache, cache_seqlens, o=None, lse=None, num_splits=None, scale=None,
                    workspace=None, stream=None, want_lse=True):
     """Split-KV decode through ``fa_fwd_kvcache``.
@@ -426,7 +434,8 @@ def _append_common(q, k_new, v_new, cache_seqlens, Hkv, d, cap, o, lse, num_spli
     if tuple(cache_seqlens.shape) != (B,):
         raise ValueError("cache_seqlens must be (B,)")
     if num_splits is None:
-        num_splits = fa_kvcache_default_splits(B, Hkv, cap, d)
+        num_splits = (fa_kvcache_default_splits(B, Hkv, cap, d) if Nq == 1 and k_new is None
+                      else fa_kvcache_append_default_splits(B, Nq, Hkv, Hq, cap, d))
     if o is None:
         o = torch.empty_like(q)
     _check(o, "o", torch.bfloat16, q.device)

@@ -178,29 +178,57 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits) {
   return fa::decode_workspace_bytes(B, Hq, d, num_splits);
 }
 
+namespace {
+
+int current_cus() {
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess)
+    return prop.multiProcessorCount;
+  (void)hipGetLastError();
+  return 256;
+}
+
+}  // namespace
+
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu) {
   if (B <= 0 || Hkv <= 0 || capacity <= 0) return 1;
-  if (num_cus <= 0) {
-    int dev = 0;
-    hipDeviceProp_t prop;
-    if (hipGetDevice(&dev) == hipSuccess && hipGetDeviceProperties(&prop, dev) == hipSuccess) {
-      num_cus = prop.multiProcessorCount;
-    } else {
-      num_cus = 256;
-    }
-  }
+  if (num_cus <= 0) num_cus = current_cus();
   if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_resident_per_cu(d);
-  // Splits of about 1024 keys keep each decode wavefront's stream long
-  // enough to amortise its pipeline start (measured best on MI355X against
-  // 512 and 768), and enough of them give every CU `wgs_per_cu` resident
-  // wavefronts.
-  const long by_len = (capacity + 1023) / 1024;
+  // The balanced decode runs (num_splits - 1) B Hkv equal runs of cache
+  // tiles: enough runs to give every resident workgroup one, each run at
+  // least about 8 tiles of 64 keys long so its start is amortised. With
+  // four or more pairs per resident slot, or a cache of one tile, one pass
+  // per pair without a combine is as balanced.
+  const long slots = (long)num_cus * wgs_per_cu;
   const long pairs = (long)B * Hkv;
-  const long by_fill = ((long)num_cus * wgs_per_cu + pairs - 1) / pairs;
+  const long tiles = ((long)capacity + 63) / 64;
+  if (pairs >= 4 * slots || tiles <= 1) return 1;
+  long per_pair = (slots + pairs - 1) / pairs;
+  const long by_len = tiles / 8 > 1 ? tiles / 8 : 1;
+  if (per_pair > by_len) per_pair = by_len;
+  long s = 1 + per_pair;
+  if (s > 65535) s = 65535;
+  return (int)s;
+}
+
+int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacity, int d, int num_cus,
+                                     int wgs_per_cu) {
+  if (B <= 0 || Nq <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || capacity <= 0) return 1;
+  if (num_cus <= 0) num_cus = current_cus();
+  if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_split_resident_per_cu(d);
+  // Splits of about 1024 keys keep each split workgroup's stream long
+  // enough to amortise its start (measured best on MI355X against 512 and
+  // 768), and enough of them give every CU `wgs_per_cu` resident
+  // workgroups; a workgroup serves 16 (query, query head) columns.
+  const long groups = ((long)Nq * (Hq / Hkv) + 15) / 16;
+  const long by_len = (capacity + 1023) / 1024;
+  const long items = (long)B * Hkv * groups;
+  const long by_fill = ((long)num_cus * wgs_per_cu + items - 1) / items;
   long s = by_len > by_fill ? by_len : by_fill;
-  // beyond ~64 waves per resident slot the extra splits only add combine work
-  const long max_waves = 64L * num_cus * wgs_per_cu;
-  if (pairs * s > max_waves) s = max_waves / pairs;
+  // beyond ~64 workgroups per resident slot the extra splits only add combine work
+  const long max_wgs = 64L * num_cus * wgs_per_cu;
+  if (items * s > max_wgs) s = max_wgs / items;
   const long max_s = (capacity + 63) / 64;  // at least one 64-key block per split
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;

@@ -109,6 +109,84 @@ struct DecTile {
   static_assert(T % 32 == 0 && TILE % 1024 == 0 && (NST - 1) * 2 * DMA <= 63, "tile shape");
 };
 
+// One T-key tile of the decode: S^T = K Q^T on the 16x16x32 MFMA (the
+// query heads of one key/value head as columns), online softmax, then
+// O^T += V^T P^T, with K and V in the ring stage at LDS address `stg`.
+// When MASK, key 16 tb + i of this lane is visible iff 16 tb + i <= lim.
+template <int D, class TL, bool MASK>
+__device__ __forceinline__ void dec_tile(f32x4 (&acc)[D / 16], float& m, float& l, const bf16x8 (&qf)[D / 32],
+                                         const uint32_t (&k_off)[D / 32], const uint32_t (&v_off)[D / 16],
+                                         uint32_t stg, int lim, float c) {
+  constexpr int T = TL::T;
+  // S^T: T keys x 16 columns, lane (col, g4) holds keys 16 tb + 4 g4 + i
+  f32x4 sc[T / 16];
+#pragma unroll
+  for (int tb = 0; tb < T / 16; ++tb) {
+    sc[tb] = f32x4{};
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) {
+      const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)(stg + k_off[ks] + tb * 16 * D * 2);
+      sc[tb] = mfma16x16x32(kf, qf[ks], sc[tb]);
+    }
+  }
+  if constexpr (MASK) {
+#pragma unroll
+    for (int tb = 0; tb < T / 16; ++tb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (16 * tb + i > lim) sc[tb][i] = -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int tb = 0; tb < T / 16; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tb][i]);
+  mx = quarters_max(mx);
+  const float m_cand = fmaxf(m, mx * c);
+  // move the reference max only when it grew by more than kSlack (see the
+  // prefill kernel: O = acc / l does not depend on the reference)
+  const bool rescale = __builtin_amdgcn_ballot_w64(m_cand > m + kSlack) != 0;
+  float alpha = 1.f;
+  if (rescale) {
+    const float mu = (m_cand == -INFINITY) ? 0.f : m_cand;
+    alpha = exp2_fast(m - mu);
+    l *= alpha;
+    m = m_cand;
+  }
+  const float m_use = (m == -INFINITY) ? 0.f : m;
+  float rs = 0.f;
+#pragma unroll
+  for (int tb = 0; tb < T / 16; ++tb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sc[tb][i] = exp2_fast(fmaf(sc[tb][i], c, -m_use));
+      rs += sc[tb][i];
+    }
+  l += rs;
+  // branch-free (alpha is 1 when nothing moved): keeps the accumulator's
+  // loop-carried registers free of conditional copies
+#pragma unroll
+  for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
+  // O^T += V^T P^T over 32-key steps: registers 0..3 hold keys 32 kk + 4 g4 + r,
+  // 4..7 keys 32 kk + 16 + 4 g4 + r
+#pragma unroll
+  for (int kk = 0; kk < T / 32; ++kk) {
+    u32x4 w;
+    w[0] = pack_bf16x2(sc[2 * kk][0], sc[2 * kk][1]);
+    w[1] = pack_bf16x2(sc[2 * kk][2], sc[2 * kk][3]);
+    w[2] = pack_bf16x2(sc[2 * kk + 1][0], sc[2 * kk + 1][1]);
+    w[3] = pack_bf16x2(sc[2 * kk + 1][2], sc[2 * kk + 1][3]);
+    const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) {
+      const i16x4 v0 = ds_read_tr(stg + v_off[dt] + kk * 32 * D * 2);
+      const i16x4 v1 = ds_read_tr(stg + v_off[dt] + (kk * 32 + 16) * D * 2);
+      const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+      acc[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pf, acc[dt]);
+    }
+  }
+}
+
 // One wavefront per (split, key/value head, sequence). The wavefront keeps
 // an NST-stage LDS ring of K/V tiles filled by direct-to-LDS loads and needs
 // no barrier: it waits for its own loads (vmcnt) before reading a stage.
@@ -229,76 +307,8 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
   float m = -INFINITY, l = 0.f;
 
   auto compute_tile = [&](int t, auto mask_tag) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    const uint32_t stg = lds0 + (uint32_t)((t % NST) * TL::STAGE);
-    // S^T: T keys x 16 columns, lane (col, g4) holds keys 16 tb + 4 g4 + i
-    f32x4 sc[T / 16];
-#pragma unroll
-    for (int tb = 0; tb < T / 16; ++tb) {
-      sc[tb] = f32x4{};
-#pragma unroll
-      for (int ks = 0; ks < D / 32; ++ks) {
-        const bf16x8 kf = *(const LDS3 bf16x8*)(uintptr_t)(stg + k_off[ks] + tb * 16 * D * 2);
-        sc[tb] = mfma16x16x32(kf, qf[ks], sc[tb]);
-      }
-    }
-    if constexpr (MASK) {
-      const int lim = climit - t * T - 4 * g4;  // key offset 16 tb + i visible iff <= lim
-#pragma unroll
-      for (int tb = 0; tb < T / 16; ++tb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (16 * tb + i > lim) sc[tb][i] = -INFINITY;
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tb = 0; tb < T / 16; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[tb][i]);
-    mx = quarters_max(mx);
-    const float m_cand = fmaxf(m, mx * p.c);
-    // move the reference max only when it grew by more than kSlack (see the
-    // prefill kernel: O = acc / l does not depend on the reference)
-    const bool rescale = __builtin_amdgcn_ballot_w64(m_cand > m + kSlack) != 0;
-    float alpha = 1.f;
-    if (rescale) {
-      const float mu = (m_cand == -INFINITY) ? 0.f : m_cand;
-      alpha = exp2_fast(m - mu);
-      l *= alpha;
-      m = m_cand;
-    }
-    const float m_use = (m == -INFINITY) ? 0.f : m;
-    float rs = 0.f;
-#pragma unroll
-    for (int tb = 0; tb < T / 16; ++tb)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sc[tb][i] = exp2_fast(fmaf(sc[tb][i], p.c, -m_use));
-        rs += sc[tb][i];
-      }
-    l += rs;
-    // branch-free (alpha is 1 when nothing moved): keeps the accumulator's
-    // loop-carried registers free of conditional copies
-#pragma unroll
-    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= alpha;
-    // O^T += V^T P^T over 32-key steps: registers 0..3 hold keys 32 kk + 4 g4 + r,
-    // 4..7 keys 32 kk + 16 + 4 g4 + r
-#pragma unroll
-    for (int kk = 0; kk < T / 32; ++kk) {
-      u32x4 w;
-      w[0] = pack_bf16x2(sc[2 * kk][0], sc[2 * kk][1]);
-      w[1] = pack_bf16x2(sc[2 * kk][2], sc[2 * kk][3]);
-      w[2] = pack_bf16x2(sc[2 * kk + 1][0], sc[2 * kk + 1][1]);
-      w[3] = pack_bf16x2(sc[2 * kk + 1][2], sc[2 * kk + 1][3]);
-      const bf16x8 pf = __builtin_bit_cast(bf16x8, w);
-#pragma unroll
-      for (int dt = 0; dt < D / 16; ++dt) {
-        const i16x4 v0 = ds_read_tr(stg + v_off[dt] + kk * 32 * D * 2);
-        const i16x4 v1 = ds_read_tr(stg + v_off[dt] + (kk * 32 + 16) * D * 2);
-        const i16x8 vv = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
-        acc[dt] = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pf, acc[dt]);
-      }
-    }
+    dec_tile<D, TL, decltype(mask_tag)::value>(acc, m, l, qf, k_off, v_off, lds0 + (uint32_t)((t % NST) * TL::STAGE),
+                                               climit - t * T - 4 * g4, p.c);
   };
 
   auto wait_tile = [&](int t) {
@@ -416,6 +426,339 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int ro
     p.lse[((int64_t)b * p.Hq + hq) * p.Nq + qi] = wsum > 0.f ? (Mu + log2_fast(wsum)) * kLn2 : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// Balanced split for one query per sequence (no append). The cache work is
+// the list of tiles of every (sequence b, key/value head h) pair, in that
+// order: pair (b, h) holds n_b = ceil(L_b / T) tiles, at flat positions
+// Hkv P(b) + h n_b .. + n_b - 1 with P(b) = n_0 + .. + n_(b-1). The U
+// units of the launch take equal runs of it: unit u covers flat tiles
+// [floor(u A / U), floor((u+1) A / U)), A the total, so every wavefront
+// streams the same number of cache bytes whatever the lengths (the split
+// of the cache over thread blocks that the pyshine.com code tour, "Why You
+// Need This", describes for decode, with its pieces cut by work rather
+// than by position). A unit writes one partial (O, LSE) per pair its run
+// touches, at slot u + Hkv NZ(b) + h (NZ(b) = sequences before b that hold
+// keys); the slots of one pair are consecutive, and the combine kernel
+// finds them from the same prefix sums.
+// ---------------------------------------------------------------------------
+
+// Tiles of sequence b per key/value head, from a scalar load of its length.
+template <int T>
+__device__ __forceinline__ int lean_tiles_uniform(const DecParams& p, int b) {
+  const __attribute__((address_space(4))) int32_t* lens =
+      (const __attribute__((address_space(4))) int32_t*)p.lens;
+  return (min(max(lens[b], 0), p.capacity) + T - 1) / T;
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Sum over all sequences of n_b (per key/value head), by one wavefront.
+template <int T>
+__device__ __forceinline__ int64_t lean_total(const DecParams& p, int B, int lane) {
+  int64_t tot = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    int n = b < B ? (min(max(p.lens[b], 0), p.capacity) + T - 1) / T : 0;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
+    tot += n;
+  }
+  return tot;
+}
+
+// The sequence holding flat tile `target` (< Hkv * total): b, n_b, P(b) and
+// NZ(b), wave-uniform.
+struct LeanSeq {
+  int b, nb;
+  int64_t pre;  // P(b)
+  int nz;       // NZ(b)
+};
+template <int T>
+__device__ __forceinline__ LeanSeq lean_locate(const DecParams& p, int B, int64_t target, int lane) {
+  int64_t pre = 0;
+  int nz = 0;
+  for (int b0 = 0; b0 < B; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < B ? (min(max(p.lens[b], 0), p.capacity) + T - 1) / T : 0;
+    const int incl = wave_incl_scan(n, lane);
+    const int nzi = wave_incl_scan(n > 0 ? 1 : 0, lane);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(b < B && (int64_t)p.Hkv * (pre + incl) > target);
+    if (hit != 0) {
+      const int j = __builtin_amdgcn_readfirstlane(__builtin_ctzll(hit));
+      LeanSeq r;
+      r.b = b0 + j;
+      r.nb = __builtin_amdgcn_readfirstlane(__shfl(n, j, 64));
+      const int64_t pr = pre + __shfl(incl, j, 64) - r.nb;
+      r.pre = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)pr) |
+              ((int64_t)__builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)pr >> 32)) << 32);
+      r.nz = __builtin_amdgcn_readfirstlane(nz + __shfl(nzi, j, 64) - (r.nb > 0 ? 1 : 0));
+      return r;
+    }
+    pre += __shfl(incl, 63, 64);
+    nz += __shfl(nzi, 63, 64);
+  }
+  return LeanSeq{B, 0, pre, nz};  // not reached for target < Hkv * total
+}
+
+// unit of flat tile t: the largest u with floor(u A / U) <= t
+__device__ __forceinline__ int64_t lean_unit_of(int64_t t, int64_t A, int64_t U) {
+  return ((t + 1) * U - 1) / A;
+}
+
+template <int D, class TL>
+__global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, int64_t U) {
+  constexpr int T = TL::T, CPR = TL::CPR;
+  static_assert(TL::NST == 2, "the lean decode keeps one tile in flight");
+  constexpr int QBYTES = kMaxGroup * D * 2;  // room for the largest group's query rows
+  __shared__ __attribute__((aligned(1024))) char smem[2 * TL::STAGE + 2 * QBYTES];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(LDS3 char*)smem;
+  const uint32_t qlds = lds0 + 2 * TL::STAGE;
+
+  const int lane = threadIdx.x;
+  const int col = lane & 15;
+  const int g4 = lane >> 4;
+  const int G = p.group;
+  const int Hkv = p.Hkv;
+  const int64_t u = blockIdx.x;
+
+  const int64_t A = (int64_t)Hkv * lean_total<T>(p, B, lane);
+  if (A == 0) return;
+  // run [t0, t1) of this unit; A = q U + r keeps the products in range
+  const int64_t qa = A / U, ra = A % U;
+  const int64_t t0 = qa * u + (ra * u) / U;
+  const int64_t t1 = qa * (u + 1) + (ra * (u + 1)) / U;
+  if (t0 >= t1) return;
+  const int count = (int)(t1 - t0);
+
+  // cursor: tile i of pair (b, h); nb = n_b, nz = NZ(b)
+  struct Cur {
+    int b, h, i, nb, nz;
+  };
+  Cur cc;
+  {
+    const LeanSeq sq = lean_locate<T>(p, B, t0, lane);
+    const int64_t r = t0 - (int64_t)Hkv * sq.pre;
+    cc.b = sq.b;
+    cc.nb = sq.nb;
+    cc.nz = sq.nz;
+    cc.h = (int)(r / sq.nb);
+    cc.i = (int)(r - (int64_t)cc.h * sq.nb);
+  }
+  wait_vm_loads();  // the lengths read above have landed before the tile loads start
+  auto advance = [&](Cur& c) {
+    if (++c.i < c.nb) return;
+    c.i = 0;
+    if (++c.h < Hkv) return;
+    c.h = 0;
+    c.nz += 1;
+    do {
+      ++c.b;
+      c.nb = c.b < B ? lean_tiles_uniform<T>(p, c.b) : 1;
+    } while (c.nb == 0);
+  };
+
+  const int kv_row = Hkv * D * 2;
+  constexpr int QD = (QBYTES + 1023) / 1024;  // at most this many 16-byte loads per lane for the query rows
+  const int qbytes = G * D * 2;
+  const int qd = (qbytes + 1023) / 1024;
+  int dma_row[TL::DMA], dma_col[TL::DMA];
+#pragma unroll
+  for (int j = 0; j < TL::DMA; ++j) {
+    const int slot = j * 64 + lane;
+    dma_row[j] = slot / CPR;
+    dma_col[j] = ((slot % CPR) ^ swz<CPR>(slot / CPR)) * 16;
+  }
+  // tile k of the run (cursor c) into stage k % 2; a tile that starts a
+  // pair is preceded by the pair's query rows (G x D, contiguous in q) into
+  // query buffer `qb`
+  auto issue = [&](const Cur& c, int k, int qb) {
+    if (c.i == 0 || k == 0) {
+      const char* qs = p.q + ((int64_t)c.b * p.Hq + (int64_t)c.h * G) * D * 2;
+#pragma unroll
+      for (int j = 0; j < QD; ++j)
+        if (j < qd) dma16(qs, (uint32_t)min((j * 64 + lane) * 16, qbytes - 16), qlds + qb * QBYTES + j * 1024);
+    }
+    const int len = c.i == c.nb - 1 ? min(max(((const __attribute__((address_space(4))) int32_t*)p.lens)[c.b], 0),
+                                          p.capacity)
+                                    : (c.i + 1) * T;
+    const int last = len - 1 - c.i * T;  // rows past the end re-read the last key (masked later)
+    const int64_t row = cache_row_uniform(p, c.b, c.i * T);
+    const char* ks = p.kc + (row * Hkv + c.h) * D * 2;
+    const char* vs = p.vc + (row * Hkv + c.h) * D * 2;
+    const uint32_t st = lds0 + (uint32_t)((k & 1) * TL::STAGE);
+#pragma unroll
+    for (int j = 0; j < TL::DMA; ++j)
+      dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
+#pragma unroll
+    for (int j = 0; j < TL::DMA; ++j)
+      dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
+  };
+
+  uint32_t k_off[D / 32];
+  {
+    const int sw = swz<CPR>(col);
+#pragma unroll
+    for (int ks = 0; ks < D / 32; ++ks) k_off[ks] = (uint32_t)(col * D * 2 + (((4 * ks + g4) ^ sw) * 16));
+  }
+  uint32_t v_off[D / 16];
+  {
+    const int row = 4 * g4 + (col >> 2);
+    const int sw = swz<CPR>(row);
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt)
+      v_off[dt] = (uint32_t)(TL::TILE + row * D * 2 + (col & 1) * 8 + (((2 * dt + ((col & 3) >> 1)) ^ sw) * 16));
+  }
+
+  bf16x8 qf[D / 32];
+  f32x4 acc[D / 16];
+  float m = -INFINITY, l = 0.f;
+  const bool cvalid = col < G;
+  int qbuf = 0;  // query buffer of the pair being computed
+
+  Cur ic = cc;  // issue cursor, one tile ahead
+  issue(ic, 0, 0);
+  int ibuf = 0;  // query buffer of the pair the issue cursor is in
+  for (int k = 0; k < count; ++k) {
+    bool next_new = false;
+    if (k + 1 < count) {
+      advance(ic);
+      next_new = ic.i == 0;
+      if (next_new) ibuf ^= 1;
+      issue(ic, k + 1, ibuf);
+    }
+    // tile k (and its pair's query rows) landed: at most tile k + 1's loads remain
+    if (k + 1 < count) {
+      if (next_new) {
+        static_for<QD + 1>([&](auto Q) {
+          if (qd == decltype(Q)::value) wait_vmcnt<2 * TL::DMA + decltype(Q)::value>();
+        });
+      } else {
+        wait_vmcnt<2 * TL::DMA>();
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    const bool seg_start = k == 0 || cc.i == 0;
+    if (seg_start) {
+      // this pair's query rows: column col is query head h G + col
+#pragma unroll
+      for (int ks = 0; ks < D / 32; ++ks) {
+        const bf16x8 x = *(const LDS3 bf16x8*)(uintptr_t)(qlds + qbuf * QBYTES + (col * D + ks * 32 + g4 * 8) * 2);
+        qf[ks] = cvalid ? x : bf16x8{};
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
+      m = -INFINITY;
+      l = 0.f;
+    }
+    const uint32_t stg = lds0 + (uint32_t)((k & 1) * TL::STAGE);
+    const bool last_of_pair = cc.i == cc.nb - 1;
+    if (last_of_pair) {
+      const int len = min(max(((const __attribute__((address_space(4))) int32_t*)p.lens)[cc.b], 0), p.capacity);
+      dec_tile<D, TL, true>(acc, m, l, qf, k_off, v_off, stg, len - 1 - cc.i * T - 4 * g4, p.c);
+    } else {
+      dec_tile<D, TL, false>(acc, m, l, qf, k_off, v_off, stg, 0, p.c);
+    }
+    if (last_of_pair || k + 1 == count) {
+      // this run's part of the pair: normalised O and base-2 LSE
+      const float lt = quarters_sum(l);
+      const int64_t slot = u + (int64_t)Hkv * cc.nz + cc.h;
+      if (cvalid) {
+        const float inv = lt > 0.f ? 1.f / lt : 0.f;
+        float* po = p.part_o + (slot * G + col) * D;
+#pragma unroll
+        for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g4) = acc[dt] * inv;
+        if (g4 == 0) p.part_lse[slot * G + col] = lt > 0.f ? m + log2_fast(lt) : -INFINITY;
+      }
+    }
+    // the query buffer a new pair's rows went into
+    const bool next_starts = k + 1 < count && last_of_pair;
+    advance(cc);
+    if (next_starts) qbuf ^= 1;
+  }
+}
+
+// One wavefront per (sequence, query head): merge the parts of its pair in
+// unit order with weights 2^(L_s - max L).
+template <int D, int T>
+__global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, int B, int64_t U) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
+  if (row >= B * p.Hq) return;
+  const int b = row / p.Hq, hq = row - b * p.Hq;
+  const int G = p.group;
+  const int h = hq / G, g = hq - h * G;
+  const int64_t A = (int64_t)p.Hkv * lean_total<T>(p, B, lane);
+  // P(b), n_b and NZ(b) from the same scan the units used
+  int64_t pre = 0;
+  int nz = 0, nb = 0;
+  for (int b0 = 0; b0 <= b; b0 += 64) {
+    const int bb = b0 + lane;
+    const int n = bb < B ? (min(max(p.lens[bb], 0), p.capacity) + T - 1) / T : 0;
+    const int incl = wave_incl_scan(bb < b ? n : 0, lane);
+    const int nzi = wave_incl_scan(bb < b && n > 0 ? 1 : 0, lane);
+    if (b < b0 + 64) nb = __shfl(n, b - b0, 64);
+    pre += __shfl(incl, 63, 64);
+    nz += __shfl(nzi, 63, 64);
+  }
+  constexpr int PER = D / 64;
+  float o[PER] = {};
+  float wsum = 0.f, M = -INFINITY;
+  if (nb > 0) {
+    const int64_t s0 = (int64_t)p.Hkv * pre + (int64_t)h * nb;
+    const int64_t u0 = lean_unit_of(s0, A, U), u1 = lean_unit_of(s0 + nb - 1, A, U);
+    const int64_t slot0 = u0 + (int64_t)p.Hkv * nz + h;
+    const int n = (int)(u1 - u0 + 1);
+    const float* pl = p.part_lse + slot0 * G + g;
+    // with more units than tiles some units own no tile and write nothing:
+    // their slots are skipped (unit u's run is empty iff its start equals
+    // the next unit's)
+    const int64_t qa = A / U, ra = A % U;
+    auto unit_start = [&](int64_t uu) { return qa * uu + (ra * uu) / U; };
+    auto has_part = [&](int s) { return A >= U || unit_start(u0 + s) < unit_start(u0 + s + 1); };
+    for (int s = lane; s < n; s += 64)
+      if (has_part(s)) M = fmaxf(M, pl[(int64_t)s * G]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    const float Mu = (M == -INFINITY) ? 0.f : M;
+    // U parts at a time, all loaded before any is used; fixed order
+    constexpr int UG = 8;
+    for (int s0p = 0; s0p < n; s0p += UG) {
+      float ls[UG], po[UG][PER];
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu) {
+        const int s = min(s0p + uu, n - 1);
+        ls[uu] = pl[(int64_t)s * G];
+        const float* src = p.part_o + ((slot0 + s) * G + g) * D + lane * PER;
+#pragma unroll
+        for (int e = 0; e < PER; ++e) po[uu][e] = src[e];
+      }
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu) {
+        if (s0p + uu < n && has_part(s0p + uu)) {
+          const float w = exp2_fast(ls[uu] - Mu);
+          wsum += w;
+#pragma unroll
+          for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[uu][e], o[e]);
+        }
+      }
+    }
+    M = Mu;
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) reinterpret_cast<bf16*>(p.o)[(int64_t)row * D + lane * PER + e] = (bf16)(o[e] * inv);
+  if (lane == 0 && p.lse != nullptr) p.lse[row] = wsum > 0.f ? (M + log2_fast(wsum)) * kLn2 : -INFINITY;
+}
+
 template <int D, class TL>
 hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   DecParams p;
@@ -457,6 +800,60 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// The balanced decode: one query per sequence, nothing appended, at least
+// two parts per pair on average (num_splits - 1 units per pair).
+template <int D, class TL>
+hipError_t launch_lean(const DecodeArgs& a, hipStream_t stream, int64_t U) {
+  DecParams p;
+  p.q = static_cast<const char*>(a.q);
+  p.kc = static_cast<char*>(const_cast<void*>(a.kcache));
+  p.vc = static_cast<char*>(const_cast<void*>(a.vcache));
+  p.lens = a.seqlens;
+  p.o = static_cast<char*>(a.o);
+  p.lse = a.lse;
+  p.Hq = a.Hq;
+  p.Hkv = a.Hkv;
+  p.group = a.Hq / a.Hkv;
+  p.capacity = a.capacity;
+  p.S = a.num_splits;
+  p.chunk = 0;
+  p.c = a.scale * kLog2e;
+  p.block_table = a.block_table;
+  p.page_size = a.page_size;
+  p.pages_per_seq = a.pages_per_seq;
+  p.num_pages = a.num_pages;
+  p.Nq = 1;
+  p.ncg = 1;
+  p.causal = 0;
+  p.n_new = 0;
+  p.kn = nullptr;
+  p.vn = nullptr;
+  p.part_o = static_cast<float*>(a.workspace);
+  p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;
+  hipLaunchKernelGGL((decode_lean_kernel<D, TL>), dim3((unsigned)U), dim3(64), 0, stream, p, a.B, U);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int rows = a.B * a.Hq;
+  hipLaunchKernelGGL((decode_lean_combine_kernel<D, TL::T>), dim3((rows + 3) / 4), dim3(256), 0, stream, p, a.B, U);
+  return hipGetLastError();
+}
+
+// Tile shape of the balanced decode per head dimension.
+template <int D>
+using LeanTile = DecTile<D, (D <= 128 ? 64 : 32), 2>;
+
+// Units of the balanced decode, or 0 where it does not apply (several
+// queries, appended rows, no split, or sizes whose unit arithmetic would
+// leave 64-bit range).
+int64_t lean_units(const DecodeArgs& a) {
+  if (a.Nq != 1 || a.k_new != nullptr || a.num_splits < 2 || a.B <= 0) return 0;
+  const int T = a.d <= 128 ? 64 : 32;
+  const int64_t U = (int64_t)(a.num_splits - 1) * a.B * a.Hkv;
+  const double tiles = (double)a.B * a.Hkv * (((double)a.capacity + T - 1) / T);
+  if (U > 0x7fffffff || tiles * (double)U >= 4.0e18) return 0;
+  return U;
+}
+
 // Tile-shape override for tuning (FA_DEC_VARIANT), read once per process.
 int dec_variant() {
   static const int v = [] {
@@ -483,12 +880,25 @@ int decode_resident_per_cu(int d) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (d) {
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTile<64>>, 64, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTile<128>>, 64, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<256, LeanTile<256>>, 64, 0); break;
+    default: break;
+  }
+  if (e != hipSuccess) (void)hipGetLastError();  // leave no sticky error behind
+  return e == hipSuccess && n > 0 ? n : 2;
+}
+
+int decode_split_resident_per_cu(int d) {
+  int n = 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (d) {
     case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<64, DecTile<64, 64, 3>>, 64, 0); break;
     case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<128, DecTile<128, 64, 2>>, 64, 0); break;
     case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_split_kernel<256, DecTile<256, 32, 2>>, 64, 0); break;
     default: break;
   }
-  if (e != hipSuccess) (void)hipGetLastError();  // leave no sticky error behind
+  if (e != hipSuccess) (void)hipGetLastError();
   return e == hipSuccess && n > 0 ? n : 2;
 }
 
@@ -500,6 +910,14 @@ bool decode_supported(int d, int group) {
 // 64-key tiles in a two-stage ring, two wavefronts per CU, beat 32-key
 // tiles in three- or four-stage rings). FA_DEC_VARIANT selects the others.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  if (const int64_t U = lean_units(a)) {
+    switch (a.d) {
+      case 64: return launch_lean<64, LeanTile<64>>(a, stream, U);
+      case 128: return launch_lean<128, LeanTile<128>>(a, stream, U);
+      case 256: return launch_lean<256, LeanTile<256>>(a, stream, U);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (a.d) {
     case 64: return launch<64, DecTile<64, 64, 3>>(a, stream);
     case 128:

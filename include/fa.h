@@ -100,13 +100,15 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
  *                j < cache_seqlens[b]. Values are clamped to [0, capacity].
  * o            : (B, 1, Hq, d) bf16, written.
  * lse          : (B, Hq) float32, written; may be NULL.
- * num_splits   : S >= 1. Split s of a sequence covers keys
- *                [s*c, min((s+1)*c, L_b)) with c = the smallest multiple of
- *                64 >= ceil(capacity / S); splits that start at or beyond
- *                L_b do no work. S == 1 writes o directly and needs no
- *                workspace; S > 1 writes per-split partial (O_s, LSE_s)
- *                into the workspace and a second kernel combines them with
- *                log-sum-exp weights.
+ * num_splits   : S >= 1. S == 1: one workgroup per (sequence, key/value
+ *                head) streams all its keys and writes o directly; no
+ *                workspace. S >= 2: the tiles of 64 keys (32 at d = 256) of
+ *                every (sequence, key/value head) pair, laid end to end in
+ *                (b, h) order, are cut into U = (S - 1) B Hkv equal runs,
+ *                one per workgroup, whatever the lengths; a run writes a
+ *                partial (O, LSE) for each pair it touches into the
+ *                workspace and a second kernel merges a pair's parts with
+ *                log-sum-exp weights, in run order.
  * workspace    : device scratch of at least
  *                fa_fwd_kvcache_workspace_size(B, Hq, d, num_splits) bytes
  *                (may be NULL when that size is 0). Contents on entry are
@@ -149,15 +151,28 @@ fa_status_t fa_fwd_kvcache_noalloc(const void* q, const void* kcache, const void
  * num_splits <= 1); 0 also for invalid sizes. */
 size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
 
-/* A num_splits for fa_fwd_kvcache on B sequences of at most `capacity`
- * keys, Hkv key/value heads and head dimension d, on a device with
- * `num_cus` compute units each holding `wgs_per_cu` resident decode
- * workgroups. Pass 0 for num_cus to use the current device's count, and 0
- * for wgs_per_cu to take it from hipOccupancyMaxActiveBlocksPerMultiprocessor
- * for the decode kernel that d selects (2 if no device can be queried).
- * Splits of about 1024 keys, at least enough splits to fill every resident
- * slot, and no more than 64 split workgroups per resident slot. Always >= 1. */
+/* A num_splits for fa_fwd_kvcache (and fa_fwd_kvcache_paged / _noalloc) on
+ * B sequences of at most `capacity` keys, Hkv key/value heads and head
+ * dimension d, on a device with `num_cus` compute units each holding
+ * `wgs_per_cu` resident decode workgroups. Pass 0 for num_cus to use the
+ * current device's count, and 0 for wgs_per_cu to take it from
+ * hipOccupancyMaxActiveBlocksPerMultiprocessor for the decode kernel that d
+ * selects (2 if no device can be queried). With num_splits = S >= 2 the
+ * single-query decode cuts the cache work of all sequences into
+ * (S - 1) B Hkv equal runs; the default gives about one run per resident
+ * workgroup, each run at least ~8 tiles of 64 keys, and 1 (no split) when
+ * there are four or more (sequence, key/value head) pairs per resident
+ * workgroup. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu);
+
+/* A num_splits for the decode calls with appended rows or several queries
+ * per sequence (fa_fwd_kvcache_append, fa_fwd_kvcache_paged_append), whose
+ * split s covers keys [s c, (s+1) c) of every sequence: splits of about 1024
+ * keys, at least enough to fill every resident workgroup (wgs_per_cu, or 0:
+ * from the occupancy API for that kernel), at most 64 workgroups per
+ * resident slot. Always >= 1 (1 also for invalid sizes). */
+int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacity, int d, int num_cus,
+                                     int wgs_per_cu);
 
 /* fa_fwd with a local window, aligned to the bottom-right corner
  * (pyshine.com FlashAttention code tour: bottom-right causal alignment

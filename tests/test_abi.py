@@ -110,12 +110,24 @@ def test_workspace_size_formula():
 
 
 def test_default_splits():
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 8      # ~1024-key splits
-    assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 96      # fill 768 resident slots
-    assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one 64-key block: cannot split
-    assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # capped by the slot budget
+    # single-query decode: about one balanced run per resident workgroup,
+    # runs of at least ~8 tiles, no split with plenty of pairs
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 2      # 512 pairs, 512 slots
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 3      # 768 slots: 2 runs per pair
+    assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 17      # capped by run length: 128 / 8 + 1
+    assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one tile: nothing to balance
+    assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # 4+ pairs per slot
     assert fa.fa_kvcache_default_splits(0, 8, 8192, 128, 256, 3) == 1
-    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 128, 256, 3) == (1000000 + 1023) // 1024
+    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 128, 256, 3) == 385
+
+
+def test_append_default_splits():
+    assert fa.fa_kvcache_append_default_splits(64, 1, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
+    assert fa.fa_kvcache_append_default_splits(1, 1, 8, 32, 8192, 128, 256, 3) == 96    # fill 768 slots
+    assert fa.fa_kvcache_append_default_splits(1, 1, 1, 1, 64, 128, 256, 3) == 1        # one block: cannot split
+    assert fa.fa_kvcache_append_default_splits(4096, 1, 8, 32, 8192, 128, 256, 3) == 1  # capped by the slot budget
+    assert fa.fa_kvcache_append_default_splits(0, 1, 8, 32, 8192, 128, 256, 3) == 1
+    assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 8    # 2 column groups per head
 
 
 def test_paged_decode_host_validation():
