@@ -8,14 +8,16 @@
 //
 // Split kernel: one wavefront per (split s, key/value head h, sequence b)
 // serves all G = Hq / Hkv query heads that read head h, so each cache byte
-// is read once. It streams its key range through a private three-stage LDS
-// ring filled by direct-to-LDS 16-byte loads (no registers stage the
-// cache, no barrier: the wavefront waits only for its own loads) and keeps
-// one online-softmax state (FlashAttention: Part 2, section 6.2). Scores
-// are S^T = K Q^T on the 16x16x32 bf16 MFMA with the G query heads as
-// columns (the other 16 - G columns are zero); P^T then feeds
+// is read once. It streams its key range through a private LDS ring of
+// key/value tiles (two stages of 64 keys at d = 128) filled by
+// direct-to-LDS 16-byte loads with the non-temporal hint (no registers
+// stage the cache, no barrier: the wavefront waits only for its own loads)
+// and keeps one online-softmax state (FlashAttention: Part 2, section 6.2).
+// Scores are S^T = K Q^T on the 16x16x32 bf16 MFMA with the G query heads
+// as columns (the other 16 - G columns are zero); P^T then feeds
 // O^T += V^T P^T from registers, the V^T operand read from the row-major V
-// tile with ds_read_b64_tr_b16.
+// tile with ds_read_b64_tr_b16. With one query per sequence and nothing
+// appended, the balanced form further down replaces the fixed splits.
 //
 // Partial results: O_s (normalised, fp32) and L_s = log2 of the split's sum
 // of 2^(t) in base-2 units; an empty split is never written, the combine
@@ -264,10 +266,10 @@ __global__ __launch_bounds__(64, 2) void decode_split_kernel(DecParams p) {
     const uint32_t st = lds0 + (uint32_t)((t % NST) * TL::STAGE);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
-      dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
+      dma16<true>(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
-      dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
+      dma16<true>(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
   };
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
@@ -596,10 +598,10 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
     const uint32_t st = lds0 + (uint32_t)((k & 1) * TL::STAGE);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
-      dma16(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
+      dma16<true>(ks, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + j * 1024);
 #pragma unroll
     for (int j = 0; j < TL::DMA; ++j)
-      dma16(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
+      dma16<true>(vs, (uint32_t)(min(dma_row[j], last) * kv_row + dma_col[j]), st + TL::TILE + j * 1024);
   };
 
   uint32_t k_off[D / 32];
@@ -711,7 +713,7 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
   }
   constexpr int PER = D / 64;
   float o[PER] = {};
-  float wsum = 0.f, M = -INFINITY;
+  float wsum = 0.f, M = -INFINITY;  // running maximum of the merged L_s
   if (nb > 0) {
     const int64_t s0 = (int64_t)p.Hkv * pre + (int64_t)h * nb;
     const int64_t u0 = lean_unit_of(s0, A, U), u1 = lean_unit_of(s0 + nb - 1, A, U);
@@ -724,12 +726,9 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
     const int64_t qa = A / U, ra = A % U;
     auto unit_start = [&](int64_t uu) { return qa * uu + (ra * uu) / U; };
     auto has_part = [&](int s) { return A >= U || unit_start(u0 + s) < unit_start(u0 + s + 1); };
-    for (int s = lane; s < n; s += 64)
-      if (has_part(s)) M = fmaxf(M, pl[(int64_t)s * G]);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    const float Mu = (M == -INFINITY) ? 0.f : M;
-    // U parts at a time, all loaded before any is used; fixed order
+    // UG parts at a time, all loaded before any is used, merged in unit
+    // order against a running maximum (one round of loads for the usual
+    // two or three parts)
     constexpr int UG = 8;
     for (int s0p = 0; s0p < n; s0p += UG) {
       float ls[UG], po[UG][PER];
@@ -741,17 +740,30 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
 #pragma unroll
         for (int e = 0; e < PER; ++e) po[uu][e] = src[e];
       }
+      // which of the UG slots hold a part: lane j answers for slot s0p + j
+      const uint64_t held = __builtin_amdgcn_ballot_w64(lane < UG && s0p + lane < n && has_part(s0p + lane));
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu)
+        if (((held >> uu) & 1) == 0) ls[uu] = -INFINITY;
+      float cm = M;
+#pragma unroll
+      for (int uu = 0; uu < UG; ++uu) cm = fmaxf(cm, ls[uu]);
+      if (cm == -INFINITY) continue;  // nothing with keys yet
+      const float r = exp2_fast(M - cm);  // 0 while M is -inf
+      wsum *= r;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) o[e] *= r;
 #pragma unroll
       for (int uu = 0; uu < UG; ++uu) {
-        if (s0p + uu < n && has_part(s0p + uu)) {
-          const float w = exp2_fast(ls[uu] - Mu);
+        if (ls[uu] != -INFINITY) {
+          const float w = exp2_fast(ls[uu] - cm);
           wsum += w;
 #pragma unroll
           for (int e = 0; e < PER; ++e) o[e] = fmaf(w, po[uu][e], o[e]);
         }
       }
+      M = cm;
     }
-    M = Mu;
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
