@@ -40,6 +40,7 @@
 
 #include "fa_device.h"
 #include "fa_launch.h"
+#include "fa_fwd_tile_asm.h"
 
 namespace fa {
 namespace {
@@ -66,9 +67,12 @@ struct FwdParams {
   float c;  // scale * log2(e)
 };
 
-template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_, bool PIPE_ = false>
+template <int D_, int BN_, int NW_, int QB_, int NST_, int WPS_, bool PIPE_ = false, bool ASM_ = false>
 struct Cfg {
   static constexpr int D = D_, BN = BN_, NW = NW_, QB = QB_, NST = NST_;
+  // one wavefront per SIMD, two query blocks per wavefront, each tile's
+  // body one hand-scheduled statement (fa_fwd_tile_asm.h)
+  static constexpr bool ASM = ASM_;
   static constexpr int WAVES_PER_SIMD = WPS_;  // register budget: 512 / WPS per lane
   // one wavefront per SIMD, two query blocks per wavefront, each tile's
   // MFMA phases overlapped with the other block's softmax (see the kernel)
@@ -528,7 +532,128 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       u_hi = min(max((fhi + 1) / BN - t0, u_lo), t_hi);
     }
   }
-  if constexpr (C::PIPE) {
+  if constexpr (C::ASM) {
+    // The hand-scheduled 64-row shape. Fixed registers between the
+    // statements below: O^T in a[0:127], the Q^T operands in a[128:191], the
+    // V^T operands in a[192:255], the next tile's K operands in v[192:255];
+    // LDS and DMA addresses enter in v[40:63]. Loads, waits and barriers of
+    // tiles this wavefront does not compute, and loads of partial tiles,
+    // stay here; each computed tile's statement waits for the next tile,
+    // passes the barrier and issues the next-but-one tile's loads itself
+    // (flags), so the next tile's K operands are read under its last MFMAs.
+    static_assert(D == 128 && BN == 64 && QB == 2 && NST == 2 && C::NW == 2 && C::DMA == 8, "assembly tile shape");
+    typedef uint32_t u32x32 __attribute__((ext_vector_type(32)));
+    typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+    typedef float f32x32 __attribute__((ext_vector_type(32)));
+    {
+      u32x32 q0, q1;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const u32x4 a = __builtin_bit_cast(u32x4, qf[0][ks]), b = __builtin_bit_cast(u32x4, qf[1][ks]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          q0[4 * ks + e] = a[e];
+          q1[4 * ks + e] = b[e];
+        }
+      }
+      asm volatile(FA_Q_TO_AGPR_ASM :: "{v[72:103]}"(q0), "{v[104:135]}"(q1) : FA_AGPR_CLOBBERS);
+      asm volatile(FA_O_ZERO_ASM ::: FA_AGPR_CLOBBERS);
+    }
+    u32x8 kaddr, vaddr, doff;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) kaddr[ks] = lds0 + k_off[ks];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vaddr[2 * dt + h] = lds0 + v_off[dt][h];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) doff[j] = dma_off[j];
+    float mA = m[0], mB = m[1], lA = l[0], lB = l[1];
+    const uint32_t dl = dma_lds;
+    // visible keys of block qb's row in tile t as lo .. lo + range relative
+    // to key (t0 + t) BN + 4 g (an empty set as lo = 2^20, range = 0)
+    auto mask_of = [&](int t, int qb, int& lo, int& range) __attribute__((always_inline)) {
+      const int my_q = qw0 + qb * 32 + r32;
+      const int base = (t0 + t) * BN + 4 * g;
+      const int l0 = (p.wl >= 0 ? my_q + off - p.wl : 0) - base;
+      const int h0 = (p.wr >= 0 ? min(my_q + off + p.wr, Nkb - 1) : Nkb - 1) - base;
+      lo = h0 >= l0 ? l0 : (1 << 20);
+      range = h0 >= l0 ? h0 - l0 : 0;
+    };
+    auto full_tile = [&](int t) __attribute__((always_inline)) { return (t0 + t + 1) * BN <= Nkb; };
+    sync_tile(0);
+    for (int t = 0; t < ntiles; ++t) {
+      if (t < t_lo || t >= t_hi) {
+        if (t + 1 < ntiles) sync_tile(t + 1);
+        continue;
+      }
+      const int stage = t & 1;
+      if (t == t_lo) {
+        if (stage == 0)
+          asm volatile(FA_KREAD_ASM_S0 :: "{v[40:47]}"(kaddr) : FA_KREAD_ASM_CLOBBERS);
+        else
+          asm volatile(FA_KREAD_ASM_S1 :: "{v[40:47]}"(kaddr) : FA_KREAD_ASM_CLOBBERS);
+      }
+      const bool dma_here = t + 2 < ntiles && full_tile(t + 2);
+      const uint32_t fl = __builtin_amdgcn_readfirstlane((t + 1 < ntiles ? 1u : 0u) | (dma_here ? 2u : 0u) |
+                                                         (t + 1 < t_hi ? 4u : 0u));
+      const int64_t nxt = (int64_t)(t0 + t + 2) * BN * kv_row;
+      const char* kb = kbase + (dma_here ? nxt : 0);
+      const char* vb = vbase + (dma_here ? nxt : 0);
+      const uint64_t kbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)kb) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)kb >> 32)) << 32);
+      const uint64_t vbu = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)vb) |
+                           ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)((uintptr_t)vb >> 32)) << 32);
+      const bool masked = t < u_lo || t >= u_hi;
+      int loA = 0, rgA = 0, loB = 0, rgB = 0;
+      if (masked) {
+        mask_of(t, 0, loA, rgA);
+        mask_of(t, 1, loB, rgB);
+      }
+      uint64_t sp;
+#define FA_TILE_OPERANDS                                                                                      \
+  : [mA] "+v"(mA), [mB] "+v"(mB), [lA] "+v"(lA), [lB] "+v"(lB), [sp] "=&s"(sp)                                \
+  : [c] "s"(p.c), [fl] "s"(fl), [dl] "s"(dl), [kb] "s"(kbu), [vb] "s"(vbu), [loA] "v"(loA), [rgA] "v"(rgA), \
+    [loB] "v"(loB), [rgB] "v"(rgB), "{v[40:47]}"(kaddr), "{v[48:55]}"(vaddr), "{v[56:63]}"(doff)            \
+  : FA_TILE_ASM_CLOBBERS
+      if (masked) {
+        if (stage == 0)
+          asm volatile(FA_TILE_ASM_S0_M FA_TILE_OPERANDS);
+        else
+          asm volatile(FA_TILE_ASM_S1_M FA_TILE_OPERANDS);
+      } else {
+        if (stage == 0)
+          asm volatile(FA_TILE_ASM_S0_U FA_TILE_OPERANDS);
+        else
+          asm volatile(FA_TILE_ASM_S1_U FA_TILE_OPERANDS);
+      }
+#undef FA_TILE_OPERANDS
+      (void)sp;
+      // a partial next-but-one tile: its clamped loads from here, after the
+      // statement's barrier
+      if (t + 2 < ntiles && !dma_here) issue_tile(t + 2);
+    }
+    {
+      f32x32 o0, o1, o2, o3;
+      asm volatile(FA_O_READ_ASM : "={v[72:103]}"(o0), "={v[104:135]}"(o1), "={v[136:167]}"(o2), "={v[168:199]}"(o3)
+                   :: FA_AGPR_CLOBBERS);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[0][0][i] = o0[i];
+        acc[0][1][i] = o0[16 + i];
+        acc[0][2][i] = o1[i];
+        acc[0][3][i] = o1[16 + i];
+        acc[1][0][i] = o2[i];
+        acc[1][1][i] = o2[16 + i];
+        acc[1][2][i] = o3[i];
+        acc[1][3][i] = o3[16 + i];
+      }
+    }
+    m[0] = mA;
+    m[1] = mB;
+    l[0] = lA;
+    l[1] = lB;
+  } else if constexpr (C::PIPE) {
     // Software pipeline of one wavefront per SIMD over two 32-row query
     // blocks A and B (64 rows), 32-key tiles. Every K and V^T operand is
     // read from LDS once per tile, held in registers, and feeds two MFMAs,
@@ -913,6 +1038,10 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     case 128:
       switch (variant()) {
         case 4: return launch<Cfg<128, 32, 2, 2, 4, 1, true>>(a, stream);
+        // the hand-scheduled 64-row shape: parity-green, measured 5-11%
+        // slower than the default (one wavefront per SIMD cannot issue the
+        // softmax's vector work fast enough beside its MFMAs)
+        case 5: return launch<Cfg<128, 64, 2, 2, 2, 1, false, true>>(a, stream);
         case 1: return launch<Cfg<128, 64, 8, 1, 2, 2>>(a, stream);
         case 2: return launch<Cfg<128, 32, 8, 1, 2, 2>>(a, stream);
         case 3: return launch<Cfg<128, 64, 8, 1, 3, 2>>(a, stream);
