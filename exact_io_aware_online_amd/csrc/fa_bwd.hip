@@ -314,7 +314,7 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
     // S^T and dP^T products n = ks NBT + nb, their K and V operands read
     // RS products ahead
     {
-      constexpr int NP = (D / 16) * NBT, RS = 4;
+      constexpr int NP = (D / 16) * NBT, RS = 8;
       bf16x8 ka[NP], va[NP];
       auto rd = [&](int n) __attribute__((always_inline)) {
         const int ks = n / NBT, nb = n % NBT;
@@ -366,7 +366,12 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
       dsf[kk] = __builtin_bit_cast(bf16x8, w);
     }
     // dQ^T += K^T dS^T, products m = dt (BN / 16) + kk, their transposed
-    // K^T operands read RA products ahead
+    // K^T operands read RA products ahead; at raised issue priority, so that
+    // of the two wavefronts on a SIMD one streams these MFMAs while the
+    // other computes its dS (with the deeper operand reads above: 1.9%
+    // faster on the causal B8 H16 N2048 backward)
+    __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_sched_barrier(0);
     {
       constexpr int NKK = BN / 16, NP = (D / 32) * NKK, RA = 4;
       i16x4 rt[NP][2];
@@ -392,6 +397,8 @@ __global__ __launch_bounds__(C::THREADS, 2) void bwd_dq_kernel(BwdParams p, int 
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_setprio(0);
   };
 
   auto sync_tile = [&](int t) __attribute__((always_inline)) {
