@@ -197,6 +197,11 @@ struct F8Cfg {
   static_assert(D == 64 || D == 128 || D == 256, "head dimension");
   static_assert(DMA >= 1 && TILE % (THREADS * 16) == 0, "tile does not split over the threads");
   static_assert(NST >= 2 && (NST - 2) * 2 * DMA <= 63, "vmcnt range");
+  // the S = K Q^T block also runs at raised issue priority: at d = 256 its 16
+  // K operand reads per MFMA chain otherwise queue behind the other wave's
+  // exponentials (about 2% on a long non-causal d = 256 prefill; neutral to
+  // slightly slower at d = 64 and 128)
+  static constexpr bool PRIO_S = D == 256;
 };
 
 // 16-byte chunk swizzle of a K tile row (D bytes = D / 16 chunks): the 16
@@ -436,7 +441,15 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
   };
 
   auto compute_tile = [&](int t, auto mask_tag, auto stage) __attribute__((always_inline)) {
-    s_phase(t, stage);
+    if constexpr (C::PRIO_S) {
+      __builtin_amdgcn_s_setprio(1);
+      __builtin_amdgcn_sched_barrier(0);
+      s_phase(t, stage);
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_s_setprio(0);
+    } else {
+      s_phase(t, stage);
+    }
     softmax_phase(t, mask_tag);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
