@@ -290,17 +290,24 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
   }
 
   // ---- per-lane LDS read offsets within a stage (the parts that vary by
-  // 32-key block nb or 16-key block kk are compile-time immediates)
+  // 32-key block nb or 16-key block kk are compile-time immediates). With
+  // 16 or more chunks per row the swizzle is below 16 and only permutes a
+  // chunk index's low four bits, so k-steps ks and ks + 8, and 32-column
+  // blocks dt and dt + 4, sit exactly 256 bytes apart: one register per
+  // residue, the rest an immediate (16 registers fewer at d = 256).
+  constexpr int NKO = (CPR >= 16 && D / 16 > 8) ? 8 : D / 16;
+  constexpr int NVO = (CPR >= 16 && D / 32 > 4) ? 4 : D / 32;
   // K (b128): row = 32 nb + r32, logical chunk 2 ks + g
-  uint32_t k_off[D / 16];
+  uint32_t k_off[NKO];
   {
     const int ksw = swz_pf<CPR>(r32);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) k_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
+    for (int ks = 0; ks < NKO; ++ks) k_off[ks] = (uint32_t)(r32 * D * 2 + (((2 * ks + g) ^ ksw) * 16));
   }
+  auto kofs = [&](int ks) __attribute__((always_inline)) { return k_off[ks % NKO] + (uint32_t)(ks / NKO) * 256u; };
   // V (transposed b64): 16-lane group grp = lane / 16 reads rows
   // 16 kk + 8 h + 4 g + (lane % 16) / 4 at columns 32 dt + 16 (grp % 2) + 4 (lane % 4)
-  uint32_t v_off[D / 32][2];
+  uint32_t v_off[NVO][2];
   {
     const int vi = lane & 15;
     const int vgrp = lane >> 4;
@@ -310,10 +317,13 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       const int row = 8 * h + 4 * (vgrp >> 1) + (vi >> 2);
       const int sw = swz_pf<CPR>(row);
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < NVO; ++dt)
         v_off[dt][h] = (uint32_t)(C::V_REGION + row * D * 2 + (vi & 1) * 8 + (((4 * dt + vcol) ^ sw) * 16));
     }
   }
+  auto vofs = [&](int dt, int h) __attribute__((always_inline)) {
+    return v_off[dt % NVO][h] + (uint32_t)(dt / NVO) * 256u;
+  };
 
   // Every wavefront takes part in every tile's wait + barrier + prefetch,
   // in order; it computes on tiles [0, nt_w), of which the first nt_full
@@ -345,7 +355,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     constexpr int NK = (D / 16) * NBT;
     constexpr int KPF = D >= 256 ? 2 : (D == 128 ? NK : (NK < 8 ? NK : 8));
     auto kread = [&](int i) __attribute__((always_inline)) {
-      return *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + k_off[i / NBT] + (i % NBT) * 32 * D * 2);
+      return *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + kofs(i / NBT) + (i % NBT) * 32 * D * 2);
     };
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -461,7 +471,7 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-        for (int h = 0; h < 2; ++h) vr[buf][kk][h] = ds_read_tr(lds0 + stg + v_off[dt][h] + kk * 16 * D * 2);
+        for (int h = 0; h < 2; ++h) vr[buf][kk][h] = ds_read_tr(lds0 + stg + vofs(dt, h) + kk * 16 * D * 2);
     };
     if constexpr (AHEAD) rd(0, 0);
 #pragma unroll
@@ -576,11 +586,11 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
     }
     u32x8 kaddr, vaddr, doff;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) kaddr[ks] = lds0 + k_off[ks];
+    for (int ks = 0; ks < 8; ++ks) kaddr[ks] = lds0 + kofs(ks);
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-      for (int h = 0; h < 2; ++h) vaddr[2 * dt + h] = lds0 + v_off[dt][h];
+      for (int h = 0; h < 2; ++h) vaddr[2 * dt + h] = lds0 + vofs(dt, h);
 #pragma unroll
     for (int j = 0; j < 8; ++j) doff[j] = dma_off[j];
     float mA = m[0], mB = m[1], lA = l[0], lB = l[1];
@@ -702,11 +712,11 @@ __global__ __launch_bounds__(C::THREADS, C::WAVES_PER_SIMD) void fwd_bf16_kernel
       return (uint32_t)__builtin_amdgcn_readfirstlane((t % NST) * C::TILE_BYTES);
     };
     auto kread = [&](uint32_t stg, int i) __attribute__((always_inline)) {
-      kf[i] = *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + k_off[i]);
+      kf[i] = *(const LDS3 bf16x8*)(uintptr_t)(lds0 + stg + kofs(i));
     };
     auto vread = [&](uint32_t stg, int i) __attribute__((always_inline)) {  // i = 0 .. 15
       const int dt = i >> 2, kk = (i >> 1) & 1, h = i & 1;
-      vr[dt][kk][h] = ds_read_tr(lds0 + stg + v_off[dt][h] + kk * 16 * D * 2);
+      vr[dt][kk][h] = ds_read_tr(lds0 + stg + vofs(dt, h) + kk * 16 * D * 2);
     };
     auto mfma_s = [&](int qb, int i) __attribute__((always_inline)) {
       sc[qb][0] = mfma32x32x16(kf[i], qf[qb][i], i == 0 ? f32x16{} : sc[qb][0]);
