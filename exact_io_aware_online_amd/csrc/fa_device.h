@@ -186,8 +186,18 @@ __device__ __forceinline__ void wait_vmcnt() {
 // lgkmcnt [11:8] = 15 (no wait on those).
 __device__ __forceinline__ void wait_vm_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Workgroup barrier after this wavefront's LDS accesses have completed
+// (s_waitcnt lgkmcnt(0), issued as a builtin so the compiler's own wait
+// insertion sees it). The wait is needed even where every LDS read's result
+// is used before the barrier in the source: the compiler may sink a read's
+// consumers (MFMAs, which touch no memory) past the barrier while the read
+// itself stays ahead of it, and that read could then still be in flight when
+// another wavefront, past the barrier, refills the same ring stage.
+// Encoding (gfx9): lgkmcnt [11:8] = 0; vmcnt [3:0], [15:14] and expcnt [6:4]
+// at their maxima (no wait).
 __device__ __forceinline__ void barrier() {
   asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

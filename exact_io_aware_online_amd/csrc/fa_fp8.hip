@@ -202,6 +202,10 @@ struct F8Cfg {
   // exponentials (about 2% on a long non-causal d = 256 prefill; neutral to
   // slightly slower at d = 64 and 128)
   static constexpr bool PRIO_S = D == 256;
+  // ring stage as an immediate LDS offset (one copy of the tile code per
+  // stage); at d = 256 the copies' register allocation keeps two versions
+  // of the accumulators, so there the stage is a register
+  static constexpr bool CONST_STAGE = D < 256;
 };
 
 // 16-byte chunk swizzle of a K tile row (D bytes = D / 16 chunks): the 16
@@ -311,23 +315,24 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
   wait_vm_loads();
   __syncthreads();  // the scale bytes are visible to every wavefront
 
-  // LDS read offsets: K operand rows in the permuted key order, V^T rows
-  uint32_t k_off[2][D / 64][2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int kr = 32 * ((r32 >> 2) & 1) + 16 * nb + 4 * (r32 >> 3) + (r32 & 3);
+  // LDS read offsets: K operand rows in the permuted key order, V^T rows.
+  // Neither swizzle looks at the row bits that the 16-key block nb (bit 4
+  // of the K row) or the 32-dimension block dt (bits 5 and up of the V^T
+  // row) set, so those blocks are a constant apart: registers for nb = 0
+  // and dt = 0, the rest immediates.
+  uint32_t k_off[D / 64][2];
+  {
+    const int kr = 32 * ((r32 >> 2) & 1) + 4 * (r32 >> 3) + (r32 & 3);
 #pragma unroll
     for (int s = 0; s < D / 64; ++s)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) k_off[nb][s][e] = (uint32_t)(kr * D + 16 * ((4 * s + 2 * g + e) ^ swz_k<D>(kr)));
+      for (int e = 0; e < 2; ++e) k_off[s][e] = (uint32_t)(kr * D + 16 * ((4 * s + 2 * g + e) ^ swz_k<D>(kr)));
   }
-  uint32_t v_off[D / 32][2];
+  auto kofs = [&](int nb, int s, int e) __attribute__((always_inline)) { return k_off[s][e] + (uint32_t)(nb * 16 * D); };
+  uint32_t v_off[2];
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) {
-    const int dim = 32 * dt + r32;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) v_off[dt][e] = (uint32_t)(C::V_REGION + dim * BN + 16 * ((2 * g + e) ^ swz_v(dim)));
-  }
+  for (int e = 0; e < 2; ++e) v_off[e] = (uint32_t)(C::V_REGION + r32 * BN + 16 * ((2 * g + e) ^ swz_v(r32)));
+  auto vofs = [&](int dt, int e) __attribute__((always_inline)) { return v_off[e] + (uint32_t)(dt * 32 * BN); };
 
   f32x16 acc[D / 32];
 #pragma unroll
@@ -357,7 +362,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
 #pragma unroll
       for (int s = 0; s < D / 64; ++s)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) kf[nb][s] = lds_read32(stg + k_off[nb][s][0], stg + k_off[nb][s][1]);
+        for (int nb = 0; nb < 2; ++nb) kf[nb][s] = lds_read32(stg + kofs(nb, s, 0), stg + kofs(nb, s, 1));
 #pragma unroll
       for (int s = 0; s < D / 64; ++s)
 #pragma unroll
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
       for (int s = 0; s < D / 64; ++s) {
         i32x8 kf[2];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) kf[nb] = lds_read32(stg + k_off[nb][s][0], stg + k_off[nb][s][1]);
+        for (int nb = 0; nb < 2; ++nb) kf[nb] = lds_read32(stg + kofs(nb, s, 0), stg + kofs(nb, s, 1));
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) sc[nb] = mfma_fp8(kf[nb], qf[s], sc[nb], ksc, qsc);
       }
@@ -433,35 +438,55 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
     const int vsc = sc_v[t];
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const i32x8 vf = lds_read32(stg + v_off[dt][0], stg + v_off[dt][1]);
+      const i32x8 vf = lds_read32(stg + vofs(dt, 0), stg + vofs(dt, 1));
       acc[dt] = mfma_fp8(vf, pf, acc[dt], vsc, 127);
       // d = 256: keep each V operand next to its MFMA (registers)
       if constexpr (D > 128) __builtin_amdgcn_sched_barrier(0);
     }
   };
 
+  // The compiler puts one wait state fewer between a scaled FP8 MFMA and a
+  // 64-bit register move (v_mov_b64) that reads its result than it puts
+  // before other vector reads (19 against 20 after
+  // v_mfma_scale_f32_32x32x64_f8f6f4). On MI355X such a move, in the
+  // accumulator copies the compiler makes where one loop hands over to the
+  // next, then read the last two rows of a block before the MFMA had
+  // written them (wrong and run-to-run different outputs). Two wait states
+  // after each MFMA phase, in inline assembly, which the compiler counts as
+  // none, put every later read of the results past its own bound.
+  auto mfma_guard = [] __attribute__((always_inline)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 1");
+    __builtin_amdgcn_sched_barrier(0);
+  };
   auto compute_tile = [&](int t, auto mask_tag, auto stage) __attribute__((always_inline)) {
     if constexpr (C::PRIO_S) {
       __builtin_amdgcn_s_setprio(1);
       __builtin_amdgcn_sched_barrier(0);
       s_phase(t, stage);
-      __builtin_amdgcn_sched_barrier(0);
+      mfma_guard();
       __builtin_amdgcn_s_setprio(0);
     } else {
+      __builtin_amdgcn_sched_barrier(0);
       s_phase(t, stage);
+      mfma_guard();
     }
     softmax_phase(t, mask_tag);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_setprio(1);
     pv_phase(t, stage);
-    __builtin_amdgcn_sched_barrier(0);
+    mfma_guard();
     __builtin_amdgcn_s_setprio(0);
   };
   auto compute_any = [&](int t, auto mask_tag) __attribute__((always_inline)) {
     const int st = t % NST;
-    static_for<NST>([&](auto S) {
-      if (st == decltype(S)::value) compute_tile(t, mask_tag, S);
-    });
+    if constexpr (C::CONST_STAGE) {
+      static_for<NST>([&](auto S) {
+        if (st == decltype(S)::value) compute_tile(t, mask_tag, S);
+      });
+    } else {
+      compute_tile(t, mask_tag, st);
+    }
   };
 
   // this wavefront's tiles: [0, u_hi) unmasked, [u_hi, t_hi) masked, the
@@ -475,11 +500,13 @@ __global__ __launch_bounds__(C::THREADS, C::WPS) void fwd_fp8_kernel(Fp8Params p
     u_hi = min((fhi + 1) / BN, t_hi);
   }
   int t = 0;
-  for (; t + NST <= u_hi; t += NST) {
-    static_for<NST>([&](auto S) {
-      sync_tile(t + decltype(S)::value);
-      compute_tile(t + decltype(S)::value, std::false_type{}, S);
-    });
+  if constexpr (C::CONST_STAGE) {
+    for (; t + NST <= u_hi; t += NST) {
+      static_for<NST>([&](auto S) {
+        sync_tile(t + decltype(S)::value);
+        compute_tile(t + decltype(S)::value, std::false_type{}, S);
+      });
+    }
   }
   for (; t < u_hi; ++t) {
     sync_tile(t);
@@ -608,7 +635,10 @@ hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t stream) {
   switch (a.d) {
     case 64: return launch_fp8<F8Cfg<64, 2, 3>>(a, stream);
     case 128: return launch_fp8<F8Cfg<128, 2, 2>>(a, stream);
-    case 256: return launch_fp8<F8Cfg<256, 2, 1>>(a, stream);
+    // two wavefronts per SIMD at every head dimension (d = 256 fits 256
+    // registers once its ring stage is a register and its LDS offsets are
+    // shared: twice as fast as one wavefront per SIMD on MI355X)
+    case 256: return launch_fp8<F8Cfg<256, 2, 2>>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
