@@ -152,6 +152,8 @@ __device__ __forceinline__ int swz_pf(int row) {
 // lds_addr + 16 l (lds_addr wave-uniform, in M0).
 // The base must be wave-uniform; it is passed through readfirstlane so the
 // compiler keeps it in SGPRs even where it cannot prove the uniformity.
+// An LDS-bound global load reads M0 one wait state after an SALU write of
+// M0 at the earliest (the compiler puts an s_nop 0 there in its own code).
 // kStream sets the non-temporal hint, for data read once (the decode's
 // key/value cache): the caches then treat the lines as streaming, which
 // lets a decode move 6-11% more bytes per second on MI355X; data that other
@@ -162,11 +164,11 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
   const uint64_t u = (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a) |
                      ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32);
   if constexpr (kStream) {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
                  :: "v"(voff), "s"((const void*)(uintptr_t)u), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                  : "memory", "m0");
   } else {
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
                  :: "v"(voff), "s"((const void*)(uintptr_t)u), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
                  : "memory", "m0");
   }

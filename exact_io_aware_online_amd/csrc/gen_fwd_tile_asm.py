@@ -348,11 +348,15 @@ def tile_body(stage, masked):
     e.raw("s_barrier")
     e.salu("s_bitcmp1_b32 %[fl], 1")
     e.salu("s_cbranch_scc0 3f")
+    # an LDS-bound global load reads M0 one wait state after the SALU write
+    # of M0 at the earliest
     for j in range(8):
         e.salu(f"s_add_u32 m0, %[dl], {stage * TILE + j * 128 * 16}")
+        e.raw("s_nop 0")
         e.raw(f"global_load_lds_dwordx4 {DMAOFF[j]}, %[kb]")
     for j in range(8):
         e.salu(f"s_add_u32 m0, %[dl], {2 * TILE + stage * TILE + j * 128 * 16}")
+        e.raw("s_nop 0")
         e.raw(f"global_load_lds_dwordx4 {DMAOFF[j]}, %[vb]")
     e.raw("3:", 0)
     e.wait_all_lds()   # (the V^T reads: already waited for by the PV_A phase)

@@ -14,6 +14,11 @@ to expose them, as wrong and run-to-run different outputs.
    MFMA's result one wait state earlier than that, and such a copy read
    stale rows on MI355X.
 
+3. Every LDS-bound global load (global_load_lds_*, whose LDS address is M0)
+   comes at least one wait state after the last scalar write of M0, as the
+   ISA's table of manually inserted wait states asks and as the compiler
+   does in its own code (s_nop 0 between the two).
+
 Paths are followed over the control-flow graph of each kernel: one wait state
 per instruction, N + 1 per s_nop N (inline assembly counted as written).
 """
@@ -186,6 +191,19 @@ def short_mfma_reads(ins, labels, bound):
     return bad
 
 
+def m0_write_then_lds_dma(ins, labels):
+    """[(index of the M0 write, the load)] where an LDS-bound global load
+    follows a scalar write of M0 with no wait state between."""
+    bad = []
+    for i, s in enumerate(ins):
+        if not re.match(r"^s_\w+\s+m0\s*,", s):
+            continue
+        for j in _successors(ins, labels, i):
+            if ins[j].split()[0].startswith("global_load_lds"):
+                bad.append((i, ins[j][:60]))
+    return bad
+
+
 @pytest.fixture(scope="module")
 def compiled(tmp_path_factory):
     if not os.path.exists(HIPCC):
@@ -238,4 +256,11 @@ def test_mfma_results_read_no_sooner_than_the_compiler_bound(compiled, src):
         r = short_mfma_reads(ins, labels[k], bound)
         if r:
             bad[k[:100]] = collections.Counter((w, n, s.split()[0]) for w, n, _, s in r)
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("src", SOURCES)
+def test_lds_dma_waits_for_its_m0_write(compiled, src):
+    funcs, labels = _functions(compiled[1][src])
+    bad = {k[:100]: r for k, ins in funcs.items() if (r := m0_write_then_lds_dma(ins, labels[k]))}
     assert not bad, bad
