@@ -28,7 +28,7 @@ sample of each workload. Prints one JSON line.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
                     [--prefill NAME] [--configs all|none|NAME,...]
                     [--no-cpu-baseline] [--splits S] [--bwd-steps N]
-                    [--fp8-steps N] [--paged-steps N] [--append-steps N]
+                    [--fp8-steps N] [--fp8-workload NAME] [--paged-steps N] [--append-steps N]
 """
 
 import argparse
@@ -210,8 +210,10 @@ def main():
     ap.add_argument("--bwd-steps", type=int, default=20,
                     help="timed fa_bwd calls on the causal training-shape workload (0 = skip)")
     ap.add_argument("--fp8-steps", type=int, default=20,
-                    help="timed FP8 forward calls (fa_fwd_fp8 on the causal training-shape workload, quantised "
-                         "with the rotation) after the step loop (0 = skip)")
+                    help="timed FP8 forward calls (fa_fwd_fp8, Q and K quantised with the rotation) after the step "
+                         "loop (0 = skip)")
+    ap.add_argument("--fp8-workload", default="mha_bf16_causal_b8_h16_n2048_d128",
+                    help="bf16 prefill workload the FP8 forward runs on (default: the causal training shape)")
     ap.add_argument("--append-steps", type=int, default=20,
                     help="timed decode-with-append calls (1 and 4 new tokens per sequence) (0 = skip)")
     ap.add_argument("--paged-steps", type=int, default=20,
@@ -373,29 +375,39 @@ def main():
     # block-quantised (timed on its own, outside the attention's clock),
     # then fa_fwd_fp8, priced against the dense FP8 peak.
     if args.fp8_steps > 0:
-        signs = SI.random_signs(wt["d"], seed=wt["seed"] + 4000).to(dev)
-        q8, qs8 = fa.fa_quantize_fp8(qt, signs=signs)
-        k8, ks8 = fa.fa_quantize_fp8(kt, signs=signs)
-        vt8, vs8 = fa.fa_quantize_fp8(vt, transpose=True)
-        o8 = torch.empty_like(qt)
-        l8 = torch.empty_like(lt)
+        wf_name = args.fp8_workload
+        wf = SI.PREFILL_WORKLOADS.get(wf_name)
+        if wf is None or wf["dtype"] != "bf16":
+            raise SystemExit(f"--fp8-workload: not a bf16 prefill workload: {wf_name}")
+        if wf_name == wt_name:
+            qf, kf, vf = qt, kt, vt
+        else:
+            qf, kf, vf = SI.prefill_inputs(device=dev, **wf)
+        scale_f = 1.0 / math.sqrt(wf["d"])
+        signs = SI.random_signs(wf["d"], seed=wf["seed"] + 4000).to(dev)
+        q8, qs8 = fa.fa_quantize_fp8(qf, signs=signs)
+        k8, ks8 = fa.fa_quantize_fp8(kf, signs=signs)
+        vt8, vs8 = fa.fa_quantize_fp8(vf, transpose=True)
+        o8 = torch.empty_like(qf)
+        l8 = torch.empty((wf["B"], wf["Hq"], wf["Nq"]), dtype=torch.float32, device=dev)
 
         def fstep():
-            fa.fa_fwd_fp8(q8, qs8, k8, ks8, vt8, vs8, wt["Nq"], wt["Nk"], causal=True, scale=scale_t, o=o8, lse=l8)
+            fa.fa_fwd_fp8(q8, qs8, k8, ks8, vt8, vs8, wf["Nq"], wf["Nk"], causal=wf["causal"], scale=scale_f, o=o8,
+                          lse=l8)
 
         def qstep():
-            fa.fa_quantize_fp8(qt, signs=signs, codes=q8, scales=qs8)
-            fa.fa_quantize_fp8(kt, signs=signs, codes=k8, scales=ks8)
-            fa.fa_quantize_fp8(vt, transpose=True, codes=vt8, scales=vs8)
+            fa.fa_quantize_fp8(qf, signs=signs, codes=q8, scales=qs8)
+            fa.fa_quantize_fp8(kf, signs=signs, codes=k8, scales=ks8)
+            fa.fa_quantize_fp8(vf, transpose=True, codes=vt8, scales=vs8)
         settle(fstep, 0.2, min_calls=3)
         f_ms = timed(fstep, args.fp8_steps)
         q_ms = timed(qstep, 10)
-        f_tf = prefill_flops(wt) / (f_ms * 1e-3) / 1e12
-        fp8 = {"workload": wt_name, "value": round(f_tf, 2), "unit": "TFLOP/s",
-               "kernel": f"fwd_fp8_kernel<{wt['d']}>", "dtype": "e4m3", "peak": PEAK_FP8_TFLOPS,
+        f_tf = prefill_flops(wf) / (f_ms * 1e-3) / 1e12
+        fp8 = {"workload": wf_name, "value": round(f_tf, 2), "unit": "TFLOP/s",
+               "kernel": f"fwd_fp8_kernel<{wf['d']}>", "dtype": "e4m3", "peak": PEAK_FP8_TFLOPS,
                "frac": round(f_tf / PEAK_FP8_TFLOPS, 4), "mean_launch_ms": round(f_ms, 5),
                "quantize_ms": round(q_ms, 5), "steps": args.fp8_steps}
-        del q8, k8, vt8, o8
+        del q8, k8, vt8, o8, qf, kf, vf
 
     # The decode workload again over a paged cache (256-row pages in a
     # shuffled pool, the same keys).
