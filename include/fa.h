@@ -44,7 +44,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, Hq % Hkv != 0, bad scale */
-  FA_ERR_UNSUPPORTED = 2, /* head_dim or dtype this build has no kernel for */
+  FA_ERR_UNSUPPORTED = 2, /* head_dim or dtype the library has no kernel for */
   FA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   FA_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch */
 } fa_status_t;
