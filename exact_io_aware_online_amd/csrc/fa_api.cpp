@@ -79,6 +79,8 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   if (!supported) return FA_ERR_UNSUPPORTED;
   // the prefill grid is one dimension of ceil(Nq / 64) * Hq * B workgroups at most
   if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  // a sequence's first query and key rows are b Nq and b Nk (32-bit)
+  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
@@ -112,6 +114,8 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!fa::fwd_bf16_supported(d)) return FA_ERR_UNSUPPORTED;
   if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  // a sequence's first query and key rows are b Nq and b Nk (32-bit)
+  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
@@ -434,6 +438,7 @@ fa_status_t bwd(const void* q, const void* k, const void* v, const void* o, cons
     return FA_ERR_UNSUPPORTED;
   const int64_t rows_q = packed ? total_q : (int64_t)B * Nq;
   const int64_t rows_k = packed ? total_k : (int64_t)B * Nk;
+  if (rows_q > 0x7fffffff || rows_k > 0x7fffffff) return FA_ERR_UNSUPPORTED;  // 32-bit row indices
   if (B == 0 || (rows_q == 0 && rows_k == 0)) return FA_OK;
   if (packed && (cu_q == nullptr || cu_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (rows_q > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))

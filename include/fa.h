@@ -80,7 +80,9 @@ const char* fa_status_string(int status);
  * key: o = 0 and lse = -inf. Rows never produce NaN from masking.
  * Returns FA_ERR_INVALID_ARG for a negative size, Hq % Hkv != 0, a null
  * q/k/v/o pointer with non-zero extent, or a bad scale; FA_ERR_UNSUPPORTED
- * for an unsupported (dtype, d).
+ * for an unsupported (dtype, d), B or Hq above 65535, or B * Nq or B * Nk
+ * above 2^31 - 1 rows (32-bit row indices; tensors themselves may exceed
+ * 2^31 elements).
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int Nq, int Nk, int d,
@@ -334,7 +336,8 @@ size_t fa_bwd_workspace_size(int B, int Hq, int Nq);
  * nothing is accumulated into them, and no atomics are used, so results
  * are bitwise reproducible.
  * Returns FA_ERR_INVALID_ARG (as fa_fwd), FA_ERR_UNSUPPORTED for d other
- * than 64 or 128 or for grids/workspaces beyond 32-bit indexing,
+ * than 64 or 128 or for grids, workspaces or row counts (B * Nq, B * Nk)
+ * beyond 32-bit indexing,
  * FA_ERR_WORKSPACE when the workspace is missing or too small. */
 fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv,

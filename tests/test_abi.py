@@ -66,6 +66,8 @@ def _fwd(**kw):
     (dict(d=512), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=fa.FA_DTYPE_F32, d=128), fa.FA_ERR_UNSUPPORTED),
     (dict(dtype=7), fa.FA_ERR_UNSUPPORTED),
+    (dict(B=2, Nq=2**30 + 64), fa.FA_ERR_UNSUPPORTED),   # 2^31 + 128 query rows
+    (dict(B=2, Nk=2**30 + 64), fa.FA_ERR_UNSUPPORTED),   # 2^31 + 128 key rows
     (dict(B=0), fa.FA_OK),          # no-op, nothing launched
     (dict(Nq=0), fa.FA_OK),         # no-op, nothing launched
 ])
@@ -158,6 +160,7 @@ def test_backward_host_validation():
     assert call(scale=0.0) == fa.FA_ERR_INVALID_ARG
     assert call(causal=2) == fa.FA_ERR_INVALID_ARG
     assert call() == fa.FA_ERR_INVALID_ARG           # null tensors
+    assert call(B=2, Nk=2**30 + 64) == fa.FA_ERR_UNSUPPORTED  # 2^31 + 128 key rows
     assert call(B=0) == fa.FA_OK
     assert fa.fa_bwd_workspace_size(2, 3, 33) == 2 * 2 * 3 * 64 * 4
     assert fa.fa_bwd_workspace_size(2, 3, 0) == 0
