@@ -192,6 +192,9 @@ FWD_CASES = [
     (1, 2, 1, 200, 333, False, 64),
     (2, 2, 2, 300, 300, True, 256),
     (1, 2, 1, 130, 257, False, 256),
+    (1, 2, 1, 64, 65536, False, 128),   # the largest key count accepted: every tile scale slot
+    (1, 1, 1, 100, 65536, False, 256),
+    (1, 2, 2, 70, 65535, False, 64),    # one short of it: a ragged last tile
 ]
 
 
