@@ -48,6 +48,16 @@ constexpr int kAbiVersion = 2;
 
 bool scale_ok(float s) { return std::isfinite(s) && s > 0.f; }
 
+// Row counts (sequence lengths, capacities, packed totals) that the launch
+// code rounds up to whole tiles in 32-bit integers: counts within 1024 of
+// INT_MAX are rejected, so that rounding never overflows.
+constexpr int kMaxRows = 0x7fffffff - 1023;
+bool rows_ok(int n) { return n <= kMaxRows; }
+
+// Device sizes given to the split policies, bounded so that their products
+// stay far inside 64-bit range.
+int clamp_count(int n, int hi) { return n > hi ? hi : n; }
+
 fa_status_t launch_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH; }
 
 }  // namespace
@@ -78,9 +88,10 @@ fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, float* 
   const bool supported = dtype == FA_DTYPE_BF16 ? fa::fwd_bf16_supported(d) : fa::fwd_f32_supported(d);
   if (!supported) return FA_ERR_UNSUPPORTED;
   // the prefill grid is one dimension of ceil(Nq / 64) * Hq * B workgroups at most
-  if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if (Hq > 65535 || B > 65535 || (((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   // a sequence's first query and key rows are b Nq and b Nk (32-bit)
-  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff || !rows_ok(Nq) || !rows_ok(Nk))
+    return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
@@ -113,9 +124,10 @@ fa_status_t fa_fwd_window(const void* q, const void* k, const void* v, void* o, 
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!fa::fwd_bf16_supported(d)) return FA_ERR_UNSUPPORTED;
-  if ((((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
+  if (Hq > 65535 || B > 65535 || (((int64_t)Nq + 63) / 64) * Hq * B > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   // a sequence's first query and key rows are b Nq and b Nk (32-bit)
-  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq > 0x7fffffff || (int64_t)B * Nk > 0x7fffffff || !rows_ok(Nq) || !rows_ok(Nk))
+    return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k == nullptr || v == nullptr)) return FA_ERR_INVALID_ARG;
@@ -148,7 +160,8 @@ fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, 
   if (Hq % Hkv != 0) return FA_ERR_INVALID_ARG;
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!fa::fwd_bf16_supported(d)) return FA_ERR_UNSUPPORTED;
-  if ((((int64_t)max_seqlen_q + 63) / 64) * Hq * B > 0x7fffffff || Hq > 65535 || B > 65535)
+  if (Hq > 65535 || B > 65535 || (((int64_t)max_seqlen_q + 63) / 64) * Hq * B > 0x7fffffff ||
+      !rows_ok(max_seqlen_q) || !rows_ok(total_q) || !rows_ok(total_k))
     return FA_ERR_UNSUPPORTED;
   if (B == 0 || max_seqlen_q == 0 || total_q == 0) return FA_OK;
   if (q == nullptr || o == nullptr || cu_seqlens_q == nullptr || cu_seqlens_k == nullptr) return FA_ERR_INVALID_ARG;
@@ -199,6 +212,8 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, 
   if (B <= 0 || Hkv <= 0 || capacity <= 0) return 1;
   if (num_cus <= 0) num_cus = current_cus();
   if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_resident_per_cu(d);
+  num_cus = clamp_count(num_cus, 1 << 16);
+  wgs_per_cu = clamp_count(wgs_per_cu, 1 << 10);
   // The balanced decode runs (num_splits - 1) B Hkv equal runs of cache
   // tiles: enough runs to give every resident workgroup one, each run at
   // least about 8 tiles of 64 keys long so its start is amortised. Where
@@ -226,19 +241,24 @@ int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacit
   if (B <= 0 || Nq <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || capacity <= 0) return 1;
   if (num_cus <= 0) num_cus = current_cus();
   if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_split_resident_per_cu(d);
+  num_cus = clamp_count(num_cus, 1 << 16);
+  wgs_per_cu = clamp_count(wgs_per_cu, 1 << 10);
   // Splits of about 1024 keys keep each split workgroup's stream long
   // enough to amortise its start (measured best on MI355X against 512 and
   // 768), and enough of them give every CU `wgs_per_cu` resident
   // workgroups; a workgroup serves 16 (query, query head) columns.
   const long groups = ((long)Nq * (Hq / Hkv) + 15) / 16;
-  const long by_len = (capacity + 1023) / 1024;
+  const long by_len = ((long)capacity + 1023) / 1024;
+  // beyond ~64 workgroups per resident slot the extra splits only add combine
+  // work; with that many (sequence, KV head, column group) items already,
+  // one split (the test avoids forming the possibly huge product)
+  const long max_wgs = 64L * num_cus * wgs_per_cu;
+  if (groups >= max_wgs || (long)B * Hkv > (max_wgs - 1) / groups) return 1;
   const long items = (long)B * Hkv * groups;
   const long by_fill = ((long)num_cus * wgs_per_cu + items - 1) / items;
   long s = by_len > by_fill ? by_len : by_fill;
-  // beyond ~64 workgroups per resident slot the extra splits only add combine work
-  const long max_wgs = 64L * num_cus * wgs_per_cu;
   if (items * s > max_wgs) s = max_wgs / items;
-  const long max_s = (capacity + 63) / 64;  // at least one 64-key block per split
+  const long max_s = ((long)capacity + 63) / 64;  // at least one 64-key block per split
   if (s > max_s) s = max_s;
   if (s < 1) s = 1;
   if (s > 65535) s = 65535;
@@ -259,7 +279,8 @@ fa_status_t kvcache(const void* q, const void* k_new, const void* v_new, const v
   if ((k_new == nullptr) != (v_new == nullptr)) return FA_ERR_INVALID_ARG;
   if (!fa::decode_supported(d, Hq / Hkv)) return FA_ERR_UNSUPPORTED;
   if (num_splits > 65535 || Hkv > 65535 || B > 65535) return FA_ERR_UNSUPPORTED;
-  if ((int64_t)B * Nq * Hq > 0x7fffffff || (int64_t)Nq * Hq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)B * Nq * Hq > 0x7fffffff || (int64_t)Nq * Hq > 0x7fffffff || !rows_ok(capacity) || !rows_ok(Nq))
+    return FA_ERR_UNSUPPORTED;
   if (B == 0) return FA_OK;
   if (q == nullptr || o == nullptr || cache_seqlens == nullptr) return FA_ERR_INVALID_ARG;
   if (capacity > 0 && (kcache == nullptr || vcache == nullptr)) return FA_ERR_INVALID_ARG;
@@ -338,7 +359,7 @@ fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* 
                                  void* stream) {
   if (page_size <= 0 || page_size % fa::kDecodePageAlign != 0 || pages_per_seq <= 0 || num_pages <= 0)
     return FA_ERR_INVALID_ARG;
-  if ((int64_t)page_size * pages_per_seq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)page_size * pages_per_seq > kMaxRows) return FA_ERR_UNSUPPORTED;
   if (B > 0 && block_table == nullptr) return FA_ERR_INVALID_ARG;
   return kvcache(q, nullptr, nullptr, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens,
                  o, lse, 0, num_splits, B, 1, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace,
@@ -352,14 +373,14 @@ fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const 
                                         void* workspace, size_t workspace_bytes, void* stream) {
   if (page_size <= 0 || page_size % fa::kDecodePageAlign != 0 || pages_per_seq <= 0 || num_pages <= 0)
     return FA_ERR_INVALID_ARG;
-  if ((int64_t)page_size * pages_per_seq > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if ((int64_t)page_size * pages_per_seq > kMaxRows) return FA_ERR_UNSUPPORTED;
   if (B > 0 && block_table == nullptr) return FA_ERR_INVALID_ARG;
   return kvcache(q, k_new, v_new, kpages, vpages, block_table, page_size, pages_per_seq, num_pages, cache_seqlens, o,
                  lse, causal, num_splits, B, Nq, Hq, Hkv, page_size * pages_per_seq, d, scale, workspace,
                  workspace_bytes, stream);
 }
 
-int fa_fp8_padded_rows(int n) { return n <= 0 ? 0 : fa::fp8_padded_rows(n); }
+int fa_fp8_padded_rows(int n) { return n <= 0 || !rows_ok(n) ? 0 : fa::fp8_padded_rows(n); }
 
 fa_status_t fa_quantize_fp8(const void* x, const float* signs, void* codes, uint8_t* scales, int transpose,
                             int B, int N, int H, int d, void* stream) {
@@ -391,7 +412,7 @@ fa_status_t fa_fwd_fp8(const void* q8, const uint8_t* q_scales, const void* k8, 
   if (!scale_ok(scale)) return FA_ERR_INVALID_ARG;
   if (!fa::fp8_fwd_supported(d)) return FA_ERR_UNSUPPORTED;
   if (Nk > fa::kFp8MaxKeys || Nq > 0x7fffffff - 128) return FA_ERR_UNSUPPORTED;
-  if ((((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff) return FA_ERR_UNSUPPORTED;
+  if (Hq > 65535 || B > 65535 || (((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff) return FA_ERR_UNSUPPORTED;
   if (B == 0 || Nq == 0) return FA_OK;
   if (q8 == nullptr || q_scales == nullptr || o == nullptr) return FA_ERR_INVALID_ARG;
   if (Nk > 0 && (k8 == nullptr || k_scales == nullptr || vt8 == nullptr || v_scales == nullptr))
@@ -438,12 +459,13 @@ fa_status_t bwd(const void* q, const void* k, const void* v, const void* o, cons
   if (!fa::bwd_supported(d)) return FA_ERR_UNSUPPORTED;
   // one-dimensional grids, and the workspace addressed with 32-bit offsets
   const int64_t nq_pad = ((int64_t)Nq + 31) / 32 * 32;
-  if ((((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff || (((int64_t)Nk + 127) / 128) * Hkv * B > 0x7fffffff ||
-      2 * (int64_t)B * Hq * nq_pad * 4 > 0xffffffffLL || Hq > 65535 || B > 65535)
+  if (Hq > 65535 || B > 65535 || (((int64_t)Nq + 127) / 128) * Hq * B > 0x7fffffff ||
+      (((int64_t)Nk + 127) / 128) * Hkv * B > 0x7fffffff || 2 * (int64_t)B * Hq * nq_pad * 4 > 0xffffffffLL)
     return FA_ERR_UNSUPPORTED;
   const int64_t rows_q = packed ? total_q : (int64_t)B * Nq;
   const int64_t rows_k = packed ? total_k : (int64_t)B * Nk;
   if (rows_q > 0x7fffffff || rows_k > 0x7fffffff) return FA_ERR_UNSUPPORTED;  // 32-bit row indices
+  if (!rows_ok(Nq) || !rows_ok(Nk) || !rows_ok(total_q) || !rows_ok(total_k)) return FA_ERR_UNSUPPORTED;
   if (B == 0 || (rows_q == 0 && rows_k == 0)) return FA_OK;
   if (packed && (cu_q == nullptr || cu_k == nullptr)) return FA_ERR_INVALID_ARG;
   if (rows_q > 0 && (q == nullptr || o == nullptr || lse == nullptr || dout == nullptr || dq == nullptr))

@@ -28,6 +28,10 @@
  *  - Errors: arguments are checked on the host before anything is
  *    enqueued; on any error nothing is written and a non-zero fa_status_t
  *    is returned. FA_ERR_LAUNCH reports a failed kernel launch.
+ *  - Sizes are ints. Sequence lengths, capacities and packed row totals
+ *    above 2^31 - 1024, grids beyond 32-bit indexing and row counts B * N
+ *    above 2^31 - 1 return FA_ERR_UNSUPPORTED; the tensors themselves may
+ *    hold more than 2^31 elements.
  *  - Thread safety: the library keeps no mutable state; concurrent calls
  *    on different streams are safe.
  */
@@ -44,7 +48,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_INVALID_ARG = 1, /* null pointer, negative size, Hq % Hkv != 0, bad scale */
-  FA_ERR_UNSUPPORTED = 2, /* head_dim or dtype the library has no kernel for */
+  FA_ERR_UNSUPPORTED = 2, /* head_dim, dtype or sizes the library has no kernel for */
   FA_ERR_WORKSPACE = 3,   /* decode workspace missing or smaller than required */
   FA_ERR_LAUNCH = 4       /* the HIP runtime rejected a kernel launch */
 } fa_status_t;
@@ -159,7 +163,8 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
  * `wgs_per_cu` resident decode workgroups. Pass 0 for num_cus to use the
  * current device's count, and 0 for wgs_per_cu to take it from
  * hipOccupancyMaxActiveBlocksPerMultiprocessor for the decode kernel that d
- * selects (2 if no device can be queried). With num_splits = S >= 2 the
+ * selects (2 if no device can be queried); counts above 65536 CUs and 1024
+ * workgroups per CU are taken as those. With num_splits = S >= 2 the
  * single-query decode cuts the cache work of all sequences into
  * (S - 1) B Hkv equal runs; the default gives about one run per resident
  * workgroup (two where one would be at least 128 tiles of 64 keys long,
@@ -272,7 +277,8 @@ fa_status_t fa_fwd_kvcache_paged_append(const void* q, const void* k_new, const 
  * exact attention, its arithmetic FP8). Quantise Q, K and V with
  * fa_quantize_fp8, then run fa_fwd_fp8 on the codes. */
 
-/* Rows of a quantised head: n rounded up to a multiple of 64 (0 for n <= 0). */
+/* Rows of a quantised head: n rounded up to a multiple of 64 (0 for n <= 0
+ * or n > 2^31 - 1024). */
 int fa_fp8_padded_rows(int n);
 
 /* Block quantisation of a bf16 tensor x (B, N, H, d) to e4m3 codes, one
@@ -306,7 +312,8 @@ fa_status_t fa_quantize_fp8(const void* x, const float* signs, void* codes, uint
  *   their scales, as fa_quantize_fp8 writes them (Nqp, Nkp = padded Nq, Nk)
  *   o   : (B, Nq, Hq, d) bfloat16     lse : (B, Hq, Nq) float32 or NULL
  * causal is top-left (key j visible to query i iff j <= i). A row that sees
- * no key gets o = 0, lse = -inf. d in {64, 128, 256}; Nk <= 65536; Hq % Hkv == 0.
+ * no key gets o = 0, lse = -inf. d in {64, 128, 256}; Nk <= 65536; B, Hq <= 65535;
+ * Hq % Hkv == 0.
  * Error codes as fa_fwd. */
 fa_status_t fa_fwd_fp8(const void* q8, const uint8_t* q_scales, const void* k8, const uint8_t* k_scales,
                        const void* vt8, const uint8_t* v_scales, void* o, float* lse,
