@@ -23,7 +23,9 @@ after its own short settle, and reported with their own rooflines under
 `configs`; then the backward, the FP8 forward (with its quantisation timed
 apart), the paged-cache decode and decode steps that append 1 or 4 new
 tokens per sequence. The CPU float64 oracle is timed last, on a bounded
-sample of each workload. Prints one JSON line.
+sample of each workload, and the outputs of the timed launches are compared
+with it on the same rows (`parity`: max-abs error of O and LSE against the
+bars 2e-2 and 1e-3). Prints one JSON line.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--settle SECONDS]
                     [--prefill NAME] [--configs all|none|NAME,...]
@@ -46,6 +48,7 @@ METRIC = "attn fwd TFLOP/s & % bf16 MFMA peak; split-KV decode HBM GB/s & % peak
 PEAK_BF16_TFLOPS = 2516.6   # 256 CU x 4096 flop/clk x 2.4 GHz (dense)
 PEAK_FP8_TFLOPS = 5033.2    # 256 CU x 8192 flop/clk x 2.4 GHz (dense)
 PEAK_HBM_GBS = 8000.0
+TOL_O, TOL_LSE = 2e-2, 1e-3  # max-abs bars of O (bf16) and LSE against the float64 oracle
 DEFAULT_PREFILL = "gqa_bf16_causal_h32kv8_n16384_d128"
 DEFAULT_DECODE = "gqa_bf16_decode_b64_h32kv8_cap8192_d128"
 # the other bf16 prefill workloads, timed after the step loop
@@ -110,14 +113,17 @@ def _host_info():
     return int(cores), cpu, blas
 
 
-def cpu_baseline(name, w, budget_s=12.0, tensors=None, block_rows=1024):
+def cpu_baseline(name, w, budget_s=12.0, tensors=None, block_rows=1024, outputs=None):
     """The CPU float64 oracle, as is, on blocks of query rows of whole
     (batch, head) slices of the same prefill workload until about
     `budget_s` seconds have passed. The oracle materialises every row's
     full score row (all Nk keys, then the mask), so its rate per row does
     not depend on which rows are taken; the rate is reported in the
     metric's accounting (the workload's algorithmic flops per query row).
-    `tensors` are the workload's (q, k, v), else they are drawn on the CPU."""
+    `tensors` are the workload's (q, k, v), else they are drawn on the CPU.
+    With `outputs` (the GPU's O and LSE of the timed launches, on the CPU)
+    the same oracle rows are compared with them; the comparison is not
+    counted in the oracle's time. Returns (baseline, parity or None)."""
     import numpy as np
     import torch
 
@@ -130,6 +136,8 @@ def cpu_baseline(name, w, budget_s=12.0, tensors=None, block_rows=1024):
     G = w["Hq"] // w["Hkv"]
     rows_done = 0
     slices = 0
+    err_o = err_l = 0.0
+    cmp_s = 0.0
     t0 = time.perf_counter()
     done = False
     for b in range(w["B"]):
@@ -139,10 +147,15 @@ def cpu_baseline(name, w, budget_s=12.0, tensors=None, block_rows=1024):
             for r0 in range(0, w["Nq"], block_rows):
                 r1 = min(r0 + block_rows, w["Nq"])
                 if w["causal"]:  # absolute row indices: the mask compares them with key positions
-                    O.attention_rows(f64(q[b:b + 1, :r1, h:h + 1]), kk, vv, True, scale, 0, 0,
-                                     rows=np.arange(r0, r1))
+                    o_ref, l_ref = O.attention_rows(f64(q[b:b + 1, :r1, h:h + 1]), kk, vv, True, scale, 0, 0,
+                                                    rows=np.arange(r0, r1))
                 else:
-                    O.attention_rows(f64(q[b:b + 1, r0:r1, h:h + 1]), kk, vv, False, scale, 0, 0)
+                    o_ref, l_ref = O.attention_rows(f64(q[b:b + 1, r0:r1, h:h + 1]), kk, vv, False, scale, 0, 0)
+                if outputs is not None:
+                    c0 = time.perf_counter()
+                    err_o = max(err_o, float(np.max(np.abs(f64(outputs[0][b, r0:r1, h]) - o_ref))))
+                    err_l = max(err_l, float(np.max(np.abs(f64(outputs[1][b, h, r0:r1]) - l_ref))))
+                    cmp_s += time.perf_counter() - c0
                 rows_done += r1 - r0
                 if time.perf_counter() - t0 >= budget_s:
                     done = True
@@ -152,19 +165,26 @@ def cpu_baseline(name, w, budget_s=12.0, tensors=None, block_rows=1024):
                 break
         if done:
             break
-    el = time.perf_counter() - t0
+    el = time.perf_counter() - t0 - cmp_s
     per_row = prefill_flops(w) / (w["B"] * w["Hq"] * w["Nq"])
     cores, cpu, blas = _host_info()
-    return {"value": per_row * rows_done / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+    base = {"value": per_row * rows_done / el / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows_done} query rows ({rows_done / w['Nq']:.2f} (batch, head) slices) of {name}, "
                       f"full fp64 score row each, {el:.1f} s",
             "cpu": cpu, "blas": blas}
+    parity = None
+    if outputs is not None:
+        parity = {"rows": rows_done, "max_abs_o": err_o, "max_abs_lse": err_l, "bar_o": TOL_O, "bar_lse": TOL_LSE,
+                  "within": err_o <= TOL_O and err_l <= TOL_LSE}
+    return base, parity
 
 
-def cpu_baseline_decode(name, w, q, kc, vc, lens, budget_s=4.0):
+def cpu_baseline_decode(name, w, q, kc, vc, lens, budget_s=4.0, outputs=None):
     """The CPU float64 oracle's decode on whole sequences (all query heads)
     of the decode workload until about `budget_s` seconds have passed;
-    GB/s over the same algorithmic bytes as the GPU figure."""
+    GB/s over the same algorithmic bytes as the GPU figure. With `outputs`
+    (the GPU's O and LSE) the same sequences are compared with them, outside
+    the oracle's time. Returns (baseline, parity or None)."""
     import numpy as np
     import torch
 
@@ -175,19 +195,31 @@ def cpu_baseline_decode(name, w, q, kc, vc, lens, budget_s=4.0):
     lens_h = lens.cpu().numpy()
     nbytes = 0
     seqs = 0
+    err_o = err_l = 0.0
+    cmp_s = 0.0
     t0 = time.perf_counter()
     for b in range(w["B"]):
         n = int(lens_h[b])
-        O.decode(f64(q[b:b + 1]), f64(kc[b:b + 1, :n]), f64(vc[b:b + 1, :n]), [n], scale)
+        o_ref, l_ref = O.decode(f64(q[b:b + 1]), f64(kc[b:b + 1, :n]), f64(vc[b:b + 1, :n]), [n], scale)
+        if outputs is not None:
+            c0 = time.perf_counter()
+            err_o = max(err_o, float(np.max(np.abs(f64(outputs[0][b, 0]) - o_ref[0]))))
+            err_l = max(err_l, float(np.max(np.abs(f64(outputs[1][b]) - l_ref[0]))))
+            cmp_s += time.perf_counter() - c0
         nbytes += n * w["Hkv"] * w["d"] * 2 * 2 + 2 * w["Hq"] * w["d"] * 2 + w["Hq"] * 4 + 4
         seqs += 1
-        if time.perf_counter() - t0 >= budget_s:
+        if time.perf_counter() - t0 - cmp_s >= budget_s:
             break
-    el = time.perf_counter() - t0
+    el = time.perf_counter() - t0 - cmp_s
     cores, cpu, blas = _host_info()
-    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
+    base = {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{seqs} of {w['B']} sequences of {name} (all query heads), fp64, {el:.1f} s",
             "cpu": cpu, "blas": blas}
+    parity = None
+    if outputs is not None:
+        parity = {"sequences": seqs, "max_abs_o": err_o, "max_abs_lse": err_l, "bar_o": TOL_O, "bar_lse": TOL_LSE,
+                  "within": err_o <= TOL_O and err_l <= TOL_LSE}
+    return base, parity
 
 
 def main():
@@ -338,7 +370,7 @@ def main():
         ms = timed(fn, args.config_launches)
         configs[name] = prefill_entry(name, w, ms, args.config_launches)
         if not args.no_cpu_baseline:
-            cpu_tensors[name] = (qx.cpu(), kx.cpu(), vx.cpu())
+            cpu_tensors[name] = ((qx.cpu(), kx.cpu(), vx.cpu()), (ox.cpu(), lx.cpu()))
         del qx, kx, vx, ox, lx
 
     # The backward of the causal training-shape workload (fa_bwd: dQ, dK,
@@ -508,12 +540,15 @@ def main():
                    "arch": getattr(props, "gcnArchName", "")},
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(args.prefill, wp, args.cpu_budget, tensors=(q.cpu(), k.cpu(), v.cpu()))
-        for name, tens in cpu_tensors.items():
-            configs[name]["cpu_baseline"] = cpu_baseline(name, SI.PREFILL_WORKLOADS[name], args.cpu_budget_other,
-                                                         tensors=tens)
-        out["decode"]["cpu_baseline"] = cpu_baseline_decode(args.decode, wd, qd, kc, vc, lens,
-                                                            args.cpu_budget_other)
+        # the oracle, timed on a sample; the timed launches' outputs are
+        # compared with it on the same rows (the "parity" entries)
+        out["cpu_baseline"], configs[args.prefill]["parity"] = cpu_baseline(
+            args.prefill, wp, args.cpu_budget, tensors=(q.cpu(), k.cpu(), v.cpu()), outputs=(o.cpu(), lse.cpu()))
+        for name, (tens, outs) in cpu_tensors.items():
+            configs[name]["cpu_baseline"], configs[name]["parity"] = cpu_baseline(
+                name, SI.PREFILL_WORKLOADS[name], args.cpu_budget_other, tensors=tens, outputs=outs)
+        out["decode"]["cpu_baseline"], out["decode"]["parity"] = cpu_baseline_decode(
+            args.decode, wd, qd, kc, vc, lens, args.cpu_budget_other, outputs=(od.cpu(), lsed.cpu()))
     print(json.dumps(out), flush=True)
 
 

@@ -57,8 +57,33 @@ def test_committed_traffic_records_are_well_formed():
 
 def test_cpu_baseline_fields_on_a_tiny_workload():
     w = dict(B=1, Hq=2, Hkv=1, Nq=64, Nk=64, d=64, causal=True, dtype="bf16", seed=1)
-    r = bench.cpu_baseline("tiny", w, budget_s=0.5)
+    r, parity = bench.cpu_baseline("tiny", w, budget_s=0.5)
+    assert parity is None
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s"
     assert r["value"] > 0 and r["cores"] >= 1
     assert "of tiny" in r["sample"]
     assert isinstance(r["cpu"], str) and isinstance(r["blas"], str)
+
+
+def test_cpu_baseline_compares_the_given_outputs():
+    # the parity entry: the oracle's rows against the outputs handed in (here
+    # the oracle's own result rounded to bf16, then one element moved)
+    import math
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as SI
+    from oracle import sdpa as O
+    w = dict(B=1, Hq=2, Hkv=1, Nq=64, Nk=64, d=64, causal=True, dtype="bf16", seed=1)
+    q, k, v = SI.prefill_inputs(device="cpu", **w)
+    scale = float(np.float32(1.0 / math.sqrt(w["d"])))
+    o_ref, l_ref = O.attention(*(t.double().numpy() for t in (q, k, v)), True, scale)
+    o = torch.from_numpy(o_ref).to(torch.bfloat16)
+    lse = torch.from_numpy(l_ref).float()
+    _, par = bench.cpu_baseline("tiny", w, budget_s=5.0, tensors=(q, k, v), outputs=(o, lse))
+    assert par["rows"] == 128 and par["within"] and par["max_abs_o"] <= 1e-2 and par["max_abs_lse"] <= 1e-6
+    o2 = o.clone()
+    o2[0, 63, 1, 5] += 0.5
+    _, par2 = bench.cpu_baseline("tiny", w, budget_s=5.0, tensors=(q, k, v), outputs=(o2, lse))
+    assert not par2["within"] and par2["max_abs_o"] >= 0.4
