@@ -1,0 +1,105 @@
+"""The hot path captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
+
+fa_fwd, fa_fwd_kvcache with a caller workspace and fa_fwd_kvcache_noalloc
+(the entry point for callers that cannot allocate, e.g. under capture) are
+recorded once and replayed several times; between replays the inputs are
+rewritten in place by ordinary eager work, and every replay must equal the
+eager calls on the same inputs bit for bit. None of the calls records a
+memset or allocates: the split partials go to the caller's workspace or to
+the library's static scratch, and every partial is written before it is read.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import seeded_inputs as SI
+from oracle import sdpa as O
+
+pytestmark = pytest.mark.gpu
+
+
+def fa():
+    import exact_io_aware_online_amd as m
+    m.lib()
+    return m
+
+
+def note(msg):
+    print(msg, flush=True)
+
+
+def f64(t):
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def test_graph_replays_equal_eager_calls():
+    m = fa()
+    dev = torch.device("cuda")
+    note("graph capture: fa_fwd + fa_fwd_kvcache + fa_fwd_kvcache_noalloc")
+    # prefill: causal GQA with ragged tiles; decode: GQA, lengths up to the capacity
+    B, Hq, Hkv, N, d = 2, 8, 2, 700, 128
+    q, k, v = SI.prefill_inputs(B=B, Hq=Hq, Hkv=Hkv, Nq=N, Nk=N, d=d, seed=81, device=dev)
+    Bd, cap = 8, 2048
+    qd, kc, vc, lens = SI.decode_inputs(Bd, Hq, Hkv, cap, d, seed=82, len_lo=1, device=dev)
+    sc = float(np.float32(1.0 / math.sqrt(d)))
+    S = m.fa_kvcache_default_splits(Bd, Hkv, cap, d)
+    assert S >= 2  # the split path, with its partials
+    ws = torch.empty(m.fa_fwd_kvcache_workspace_size(Bd, Hq, d, S), dtype=torch.uint8, device=dev)
+
+    def outputs():
+        return (torch.empty_like(q), torch.empty(B, Hq, N, dtype=torch.float32, device=dev),
+                torch.empty_like(qd), torch.empty(Bd, Hq, dtype=torch.float32, device=dev),
+                torch.empty_like(qd), torch.empty(Bd, Hq, dtype=torch.float32, device=dev))
+
+    def run(o, lse, od, lsed, on, lsen):
+        m.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=sc)
+        m.fa_fwd_kvcache(qd, kc, vc, lens, o=od, lse=lsed, num_splits=S, scale=sc, workspace=ws)
+        m.fa_fwd_kvcache_noalloc(qd, kc, vc, lens, o=on, lse=lsen, num_splits=S, scale=sc)
+
+    graph_out = outputs()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*graph_out)  # warm-up outside the capture (first-use lookups)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(*graph_out)
+    torch.cuda.synchronize()
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(83)
+    names = ("O", "LSE", "decode O", "decode LSE", "no-alloc O", "no-alloc LSE")
+    for rep in range(4):
+        # new inputs in place, by eager kernels, between replays
+        for t in (q, k, v, qd, kc, vc):
+            t.copy_(torch.randn(t.shape, generator=gen, device=dev).to(t.dtype))
+        lens.copy_(torch.randint(1, cap + 1, (Bd,), generator=gen, device=dev, dtype=torch.int32))
+        if rep == 3:
+            lens[0] = 0  # an empty sequence: O = 0, LSE = -inf
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in graph_out]
+        eager = outputs()
+        run(*eager)
+        torch.cuda.synchronize()
+        for name, a, b in zip(names, got, eager):
+            assert torch.equal(a.view(torch.int8), b.view(torch.int8)), (rep, name)
+        assert torch.equal(got[2].view(torch.int16), got[4].view(torch.int16)), (rep, "no-alloc vs workspace")
+        # and the replay is the attention of its inputs: a few rows against the oracle
+        o_ref, l_ref = O.attention_rows(f64(q[1:2, :, Hq - 1:Hq]), f64(k[1:2, :, Hkv - 1:Hkv]),
+                                        f64(v[1:2, :, Hkv - 1:Hkv]), True, sc, 0, 0, rows=np.arange(N - 40, N))
+        assert np.max(np.abs(f64(got[0][1, N - 40:, Hq - 1]) - o_ref)) <= 2e-2
+        assert np.max(np.abs(f64(got[1][1, Hq - 1, N - 40:]) - l_ref)) <= 1e-3
+        n = int(lens[Bd - 1])
+        od_ref, ld_ref = O.decode(f64(qd[Bd - 1:]), f64(kc[Bd - 1:, :n]), f64(vc[Bd - 1:, :n]), [n], sc)
+        assert np.max(np.abs(f64(got[2][Bd - 1, 0]) - od_ref[0])) <= 2e-2
+        assert np.max(np.abs(f64(got[3][Bd - 1]) - ld_ref[0])) <= 1e-3
+        note(f"  replay {rep}: equal to the eager calls; sampled rows within the oracle bars")
+    del g
+    torch.cuda.synchronize()
