@@ -1,8 +1,10 @@
 """The hot path captured in a HIP graph (torch.cuda.CUDAGraph) and replayed.
 
 fa_fwd, fa_fwd_kvcache with a caller workspace and fa_fwd_kvcache_noalloc
-(the entry point for callers that cannot allocate, e.g. under capture) are
-recorded once and replayed several times; between replays the inputs are
+(the entry point for callers that cannot allocate, e.g. under capture), and
+in a second graph fa_bwd with a caller workspace and the FP8 quantise +
+forward pipeline, are recorded once and replayed several times; between
+replays the inputs are
 rewritten in place by ordinary eager work, and every replay must equal the
 eager calls on the same inputs bit for bit. None of the calls records a
 memset or allocates: the split partials go to the caller's workspace or to
@@ -101,5 +103,67 @@ def test_graph_replays_equal_eager_calls():
         assert np.max(np.abs(f64(got[2][Bd - 1, 0]) - od_ref[0])) <= 2e-2
         assert np.max(np.abs(f64(got[3][Bd - 1]) - ld_ref[0])) <= 1e-3
         note(f"  replay {rep}: equal to the eager calls; sampled rows within the oracle bars")
+    del g
+    torch.cuda.synchronize()
+
+
+def test_graph_replays_of_backward_and_fp8_equal_eager_calls():
+    m = fa()
+    dev = torch.device("cuda")
+    note("graph capture: fa_bwd (caller workspace), fa_quantize_fp8 x3 + fa_fwd_fp8")
+    B, Hq, Hkv, N, d = 2, 4, 2, 300, 128
+    q, k, v = SI.prefill_inputs(B=B, Hq=Hq, Hkv=Hkv, Nq=N, Nk=N, d=d, seed=91, device=dev)
+    sc = float(np.float32(1.0 / math.sqrt(d)))
+    o, lse = m.fa_fwd(q, k, v, causal=True, scale=sc)
+    dout = torch.randn(q.shape, generator=torch.Generator(device=dev).manual_seed(92), device=dev).to(q.dtype)
+    bws = torch.empty(m.fa_bwd_workspace_size(B, Hq, N), dtype=torch.uint8, device=dev)
+    signs = SI.random_signs(d, seed=93, device=dev)
+    Np = m.fa_fp8_padded_rows(N)
+
+    def outputs():
+        codes = [torch.empty(B, Hq, Np, d, dtype=torch.uint8, device=dev),
+                 torch.empty(B, Hkv, Np, d, dtype=torch.uint8, device=dev),
+                 torch.empty(B, Hkv, d, Np, dtype=torch.uint8, device=dev)]
+        scales = [torch.empty(B, h, Np // 64, dtype=torch.uint8, device=dev) for h in (Hq, Hkv, Hkv)]
+        return ([torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)], codes, scales,
+                [torch.empty_like(q), torch.empty(B, Hq, N, dtype=torch.float32, device=dev)])
+
+    def run(grads, codes, scales, fo):
+        m.fa_bwd(q, k, v, o, lse, dout, causal=True, scale=sc, dq=grads[0], dk=grads[1], dv=grads[2], workspace=bws)
+        m.fa_quantize_fp8(q, signs, codes=codes[0], scales=scales[0])
+        m.fa_quantize_fp8(k, signs, codes=codes[1], scales=scales[1])
+        m.fa_quantize_fp8(v, transpose=True, codes=codes[2], scales=scales[2])
+        m.fa_fwd_fp8(codes[0], scales[0], codes[1], scales[1], codes[2], scales[2], N, N, causal=True, scale=sc,
+                     o=fo[0], lse=fo[1])
+
+    graph_out = outputs()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*graph_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(*graph_out)
+    torch.cuda.synchronize()
+
+    flat = lambda outs: [t for group in outs for t in group]
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(94)
+    for rep in range(3):
+        for t in (q, k, v, dout):
+            t.copy_(torch.randn(t.shape, generator=gen, device=dev).to(t.dtype))
+        m.fa_fwd(q, k, v, o=o, lse=lse, causal=True, scale=sc)  # the forward the backward reads
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in flat(graph_out)]
+        eager = outputs()
+        run(*eager)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(got, flat(eager))):
+            assert torch.equal(a.view(torch.int8), b.view(torch.int8)), (rep, i)
+        note(f"  replay {rep}: dq, dk, dv, the FP8 codes and scales, O and LSE equal to the eager calls")
     del g
     torch.cuda.synchronize()
