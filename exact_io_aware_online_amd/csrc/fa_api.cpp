@@ -70,7 +70,7 @@ const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG: invalid argument";
-    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim/dtype/group";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: unsupported head_dim/dtype/group/size";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: kernel launch failed";
     default: return "FA_ERR_UNKNOWN";
