@@ -216,19 +216,17 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, 
   wgs_per_cu = clamp_count(wgs_per_cu, 1 << 10);
   // The balanced decode runs (num_splits - 1) B Hkv equal runs of cache
   // tiles: enough runs to give every resident workgroup one, each run at
-  // least about 8 tiles of 64 keys long so its start is amortised. Where
-  // one run per workgroup would be 128 or more tiles long (by capacity),
-  // two per workgroup let the hardware's dispatch even out slots that
-  // stream more slowly (measured on MI355X: 1.4-3.4% faster at 128-192
-  // tiles, 4% slower at 96, equal at 64). With four or more pairs per
-  // resident slot, or a cache of one tile, one pass per pair without a
-  // combine is as balanced.
+  // least about 8 tiles of 64 keys long so its start is amortised. With
+  // four or more pairs per resident slot, or a cache of one tile, one pass
+  // per pair without a combine is as balanced. (Two runs per workgroup
+  // measured 0-1.8% faster where full caches make long runs, but up to 11%
+  // slower where the sequences are much shorter than the capacity, which
+  // is all this function knows of them.)
   const long slots = (long)num_cus * wgs_per_cu;
   const long pairs = (long)B * Hkv;
   const long tiles = ((long)capacity + 63) / 64;
   if (pairs >= 4 * slots || tiles <= 1) return 1;
-  const long runs = pairs * tiles >= 128 * slots ? 2 * slots : slots;
-  long per_pair = (runs + pairs - 1) / pairs;
+  long per_pair = (slots + pairs - 1) / pairs;
   const long by_len = tiles / 8 > 1 ? tiles / 8 : 1;
   if (per_pair > by_len) per_pair = by_len;
   long s = 1 + per_pair;

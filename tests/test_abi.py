@@ -112,14 +112,11 @@ def test_workspace_size_formula():
 
 
 def test_default_splits():
-    # single-query decode: about one balanced run per resident workgroup
-    # (two where one would be 128+ tiles long), runs of at least ~8 tiles,
-    # no split with plenty of pairs
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 3      # runs of 128 tiles: 1024 runs
-    assert fa.fa_kvcache_default_splits(64, 8, 4096, 128, 256, 2) == 2      # runs of 64 tiles: 512 runs
-    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 3      # 96 tiles: 768 runs (2 per pair)
-    assert fa.fa_kvcache_default_splits(96, 8, 8192, 128, 256, 2) == 3      # 192 tiles: 1536 runs
-    assert fa.fa_kvcache_default_splits(128, 8, 8192, 128, 256, 2) == 2     # 1024 pairs already 2 per slot
+    # single-query decode: about one balanced run per resident workgroup,
+    # runs of at least ~8 tiles, no split with plenty of pairs
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 2      # 512 pairs, 512 slots
+    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 3      # 384 pairs: 768 runs
+    assert fa.fa_kvcache_default_splits(128, 8, 8192, 128, 256, 2) == 2     # 1024 pairs, one run each
     assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 3      # 768 slots: 2 runs per pair
     assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 17      # capped by run length: 128 / 8 + 1
     assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one tile: nothing to balance

@@ -107,7 +107,7 @@ int main() {
   EXPECT(fa_fwd_kvcache_workspace_size(0, 8, 128, 4), 0);
   EXPECT(fa_fwd_kvcache_workspace_size(M, M, 256, 1), 0);
   (void)fa_fwd_kvcache_workspace_size(65535, 65535, 256, 65535);
-  EXPECT(fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2), 3);
+  EXPECT(fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2), 2);
   EXPECT(fa_kvcache_default_splits(M, M, M, 128, 256, 2), 1);
   const int big[] = {1, 2, 63, 64, 65, 1 << 20, M - 1024, M - 1, M};
   for (int a : big)
