@@ -211,7 +211,7 @@ int current_cus() {
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu) {
   if (B <= 0 || Hkv <= 0 || capacity <= 0) return 1;
   if (num_cus <= 0) num_cus = current_cus();
-  if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_resident_per_cu(d);
+  if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_resident_per_cu(d, (int64_t)B * Hkv);
   num_cus = clamp_count(num_cus, 1 << 16);
   wgs_per_cu = clamp_count(wgs_per_cu, 1 << 10);
   // The balanced decode runs (num_splits - 1) B Hkv equal runs of cache

@@ -115,10 +115,11 @@ int decode_chunk(int capacity, int num_splits);
 constexpr int kDecodePageAlign = 64;  // page sizes must be multiples of this
 size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits);
 // Resident workgroups per CU of the balanced single-query decode kernel
+// that a call with `pairs` (sequence, key/value head) pairs runs
 // (decode_resident_per_cu) and of the split kernel that serves appends and
 // several queries per sequence, for head dimension d (occupancy API; 2
 // when no device can be queried).
-int decode_resident_per_cu(int d);
+int decode_resident_per_cu(int d, int64_t pairs);
 int decode_split_resident_per_cu(int d);
 
 bool fwd_bf16_supported(int d);

@@ -5,7 +5,8 @@ draws batch size, key/value heads, group size (1 to 16 query heads per key/
 value head), head dimension, cache capacity (not always a multiple of the
 64-key tile), lengths (0 and the full capacity included) and the split
 count (1, small, large, more runs than tiles, the default) from a fixed
-numpy generator. Each case runs the contiguous decode and the same keys as a
+numpy generator, plus cases with 256 or more (sequence, key/value head)
+pairs, which take the 32-key-tile shape of the balanced decode at d = 128. Each case runs the contiguous decode and the same keys as a
 paged cache (random page size, pages scattered over a pool with spare pages)
 and compares O and LSE with the float64 oracle (O 2e-2, LSE 1e-3), and the
 paged result with the contiguous one bit for bit.
@@ -39,7 +40,22 @@ def _cases(n=24, seed=2027):
     return out
 
 
-CASES = _cases()
+def _many_pair_cases(n=10, seed=2032):
+    # at least 256 (sequence, key/value head) pairs: the 32-key-tile shape of the balanced decode at d = 128
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        hkv = int(rng.choice([4, 8]))
+        g = int(rng.choice([1, 2, 4, 8]))
+        B = int(rng.integers(256 // hkv, 256 // hkv + 40))
+        cap = int(rng.choice([64, 100, 513, 1024, 2000]))
+        S = int(rng.choice([0, 2, 3, 5]))
+        page = int(rng.choice([64, 128, 256]))
+        out.append((B, hkv * g, hkv, cap, 128, S, page, 800 + i))
+    return out
+
+
+CASES = _cases() + _many_pair_cases()
 
 
 def f64(t):
