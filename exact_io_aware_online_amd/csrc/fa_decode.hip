@@ -850,16 +850,18 @@ hipError_t launch_lean(const DecodeArgs& a, hipStream_t stream, int64_t U) {
   return hipGetLastError();
 }
 
-// Tile shape of the balanced decode per head dimension. At d = 128, calls
-// with at least kLeanSmallTilePairs (sequence, key/value head) pairs take
-// 32-key tiles (measured on MI355X, GQA with 8 KV heads: 2-4% faster from
-// 32 sequences up, 17% with short sequences; 64-key tiles stay 6-11%
-// faster at 8 sequences or fewer, whose defaults split each pair further).
+// Tile shape of the balanced decode per head dimension. At d = 64 and 128,
+// calls with at least kLeanSmallTilePairs (sequence, key/value head) pairs
+// take 32-key tiles (measured on MI355X, GQA with 8 KV heads: 2-4% faster
+// from 32 sequences up at d = 128, 17% with short sequences, 1-2% at d = 64;
+// 64-key tiles stay 6-11% faster at 8 sequences or fewer, whose defaults
+// split each pair further).
 template <int D>
 using LeanTile = DecTile<D, (D <= 128 ? 64 : 32), 2>;
-using LeanTileSmall128 = DecTile<128, 32, 2>;
+template <int D>
+using LeanTileSmall = DecTile<D, 32, 2>;
 constexpr int64_t kLeanSmallTilePairs = 256;
-bool lean_small_tiles(int d, int64_t pairs) { return d == 128 && pairs >= kLeanSmallTilePairs; }
+bool lean_small_tiles(int d, int64_t pairs) { return (d == 64 || d == 128) && pairs >= kLeanSmallTilePairs; }
 
 // Units of the balanced decode, or 0 where it does not apply (several
 // queries, appended rows, no split, or sizes whose unit arithmetic would
@@ -899,10 +901,14 @@ int decode_resident_per_cu(int d, int64_t pairs) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (d) {
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTile<64>>, 64, 0); break;
+    case 64:
+      e = lean_small_tiles(d, pairs)
+              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTileSmall<64>>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTile<64>>, 64, 0);
+      break;
     case 128:
       e = lean_small_tiles(d, pairs)
-              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTileSmall128>, 64, 0)
+              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTileSmall<128>>, 64, 0)
               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTile<128>>, 64, 0);
       break;
     case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<256, LeanTile<256>>, 64, 0); break;
@@ -935,9 +941,11 @@ bool decode_supported(int d, int group) {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   if (const int64_t U = lean_units(a)) {
     switch (a.d) {
-      case 64: return launch_lean<64, LeanTile<64>>(a, stream, U);
+      case 64:
+        return lean_small_tiles(64, (int64_t)a.B * a.Hkv) ? launch_lean<64, LeanTileSmall<64>>(a, stream, U)
+                                                         : launch_lean<64, LeanTile<64>>(a, stream, U);
       case 128:
-        return lean_small_tiles(128, (int64_t)a.B * a.Hkv) ? launch_lean<128, LeanTileSmall128>(a, stream, U)
+        return lean_small_tiles(128, (int64_t)a.B * a.Hkv) ? launch_lean<128, LeanTileSmall<128>>(a, stream, U)
                                                           : launch_lean<128, LeanTile<128>>(a, stream, U);
       case 256: return launch_lean<256, LeanTile<256>>(a, stream, U);
       default: return hipErrorInvalidValue;

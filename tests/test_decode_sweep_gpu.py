@@ -6,7 +6,8 @@ value head), head dimension, cache capacity (not always a multiple of the
 64-key tile), lengths (0 and the full capacity included) and the split
 count (1, small, large, more runs than tiles, the default) from a fixed
 numpy generator, plus cases with 256 or more (sequence, key/value head)
-pairs, which take the 32-key-tile shape of the balanced decode at d = 128. Each case runs the contiguous decode and the same keys as a
+pairs, which take the 32-key-tile shape of the balanced decode at d = 64 and
+128. Each case runs the contiguous decode and the same keys as a
 paged cache (random page size, pages scattered over a pool with spare pages)
 and compares O and LSE with the float64 oracle (O 2e-2, LSE 1e-3), and the
 paged result with the contiguous one bit for bit.
@@ -40,8 +41,8 @@ def _cases(n=24, seed=2027):
     return out
 
 
-def _many_pair_cases(n=10, seed=2032):
-    # at least 256 (sequence, key/value head) pairs: the 32-key-tile shape of the balanced decode at d = 128
+def _many_pair_cases(n=10, seed=2032, d=128):
+    # at least 256 (sequence, key/value head) pairs: the 32-key-tile shape of the balanced decode at d = 64 and 128
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
@@ -51,11 +52,11 @@ def _many_pair_cases(n=10, seed=2032):
         cap = int(rng.choice([64, 100, 513, 1024, 2000]))
         S = int(rng.choice([0, 2, 3, 5]))
         page = int(rng.choice([64, 128, 256]))
-        out.append((B, hkv * g, hkv, cap, 128, S, page, 800 + i))
+        out.append((B, hkv * g, hkv, cap, d, S, page, (800 if d == 128 else 850) + i))
     return out
 
 
-CASES = _cases() + _many_pair_cases()
+CASES = _cases() + _many_pair_cases() + _many_pair_cases(n=8, seed=2033, d=64)
 
 
 def f64(t):
