@@ -14,6 +14,12 @@
 #include "fa.h"
 #include "fa_launch.h"
 
+namespace fa {
+// Defined beside the decode kernels: whether a split decode call of these
+// sizes takes the balanced schedule.
+bool decode_balanced(int B, int Nq, int Hq, int Hkv, bool append);
+}  // namespace fa
+
 namespace {
 
 // Scratch of the allocation-free decode entry point: one copy per GPU in
@@ -237,6 +243,8 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, 
 int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacity, int d, int num_cus,
                                      int wgs_per_cu) {
   if (B <= 0 || Nq <= 0 || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || capacity <= 0) return 1;
+  // Calls that take the balanced decode use its rule, the one-query rule.
+  if (fa::decode_balanced(B, Nq, Hq, Hkv, true)) return fa_kvcache_default_splits(B, Hkv, capacity, d, num_cus, wgs_per_cu);
   if (num_cus <= 0) num_cus = current_cus();
   if (wgs_per_cu <= 0) wgs_per_cu = fa::decode_split_resident_per_cu(d);
   num_cus = clamp_count(num_cus, 1 << 16);

@@ -30,6 +30,9 @@
 #include "fa_launch.h"
 
 namespace fa {
+
+bool decode_balanced(int B, int Nq, int Hq, int Hkv, bool append);
+
 namespace {
 
 constexpr int kSplitAlign = 64;  // split boundaries are multiples of this many keys
@@ -429,27 +432,48 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecParams p, int ro
 }
 
 // ---------------------------------------------------------------------------
-// Balanced split for one query per sequence (no append). The cache work is
+// Balanced split, for calls whose queries of one sequence and key/value
+// head fit one group of 16 MFMA columns (Nq G <= 16, column qi G + g for
+// query qi and head h G + g), appended rows included. The cache work is
 // the list of tiles of every (sequence b, key/value head h) pair, in that
-// order: pair (b, h) holds n_b = ceil(L_b / T) tiles, at flat positions
+// order: pair (b, h) holds n_b = ceil(L_b / T) tiles (L_b the held plus the
+// appended rows, within capacity), at flat positions
 // Hkv P(b) + h n_b .. + n_b - 1 with P(b) = n_0 + .. + n_(b-1). The U
 // units of the launch take equal runs of it: unit u covers flat tiles
 // [floor(u A / U), floor((u+1) A / U)), A the total, so every wavefront
 // streams the same number of cache bytes whatever the lengths (the split
 // of the cache over thread blocks that the pyshine.com code tour, "Why You
 // Need This", describes for decode, with its pieces cut by work rather
-// than by position). A unit writes one partial (O, LSE) per pair its run
-// touches, at slot u + Hkv NZ(b) + h (NZ(b) = sequences before b that hold
-// keys); the slots of one pair are consecutive, and the combine kernel
-// finds them from the same prefix sums.
+// than by position). A unit writes one partial (O, LSE) per column of each
+// pair its run touches, at slot u + Hkv NZ(b) + h (NZ(b) = sequences
+// before b that hold keys); the slots of one pair are consecutive, and the
+// combine kernel finds them from the same prefix sums. The unit whose run
+// holds a tile that appended rows fall in writes them into the cache just
+// before it loads that tile, so every tile is written and read by one
+// wavefront.
 // ---------------------------------------------------------------------------
 
-// Tiles of sequence b per key/value head, from a scalar load of its length.
-template <int T>
-__device__ __forceinline__ int lean_tiles_uniform(const DecParams& p, int b) {
+// Rows a pair attends, held plus appended within capacity, for a held
+// length `len` as read from the lengths array. MQ: the call may have
+// several queries per sequence or appended rows; the one-query form is
+// compiled apart so that it carries none of their work.
+template <bool MQ>
+__device__ __forceinline__ int lean_rows(const DecParams& p, int len) {
+  if constexpr (MQ) return min(min(max(len, 0), p.capacity) + p.n_new, p.capacity);
+  return min(max(len, 0), p.capacity);
+}
+
+// Held length of sequence b by a scalar load (uniform b).
+__device__ __forceinline__ int lean_len_uniform(const DecParams& p, int b) {
   const __attribute__((address_space(4))) int32_t* lens =
       (const __attribute__((address_space(4))) int32_t*)p.lens;
-  return (min(max(lens[b], 0), p.capacity) + T - 1) / T;
+  return lens[b];
+}
+
+// Tiles of sequence b per key/value head.
+template <int T, bool MQ>
+__device__ __forceinline__ int lean_tiles_uniform(const DecParams& p, int b) {
+  return (lean_rows<MQ>(p, lean_len_uniform(p, b)) + T - 1) / T;
 }
 
 // Inclusive prefix sum over the 64 lanes.
@@ -463,12 +487,12 @@ __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
 }
 
 // Sum over all sequences of n_b (per key/value head), by one wavefront.
-template <int T>
+template <int T, bool MQ>
 __device__ __forceinline__ int64_t lean_total(const DecParams& p, int B, int lane) {
   int64_t tot = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
-    int n = b < B ? (min(max(p.lens[b], 0), p.capacity) + T - 1) / T : 0;
+    int n = b < B ? (lean_rows<MQ>(p, p.lens[b]) + T - 1) / T : 0;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) n += __shfl_xor(n, off, 64);
     tot += n;
@@ -483,13 +507,13 @@ struct LeanSeq {
   int64_t pre;  // P(b)
   int nz;       // NZ(b)
 };
-template <int T>
+template <int T, bool MQ>
 __device__ __forceinline__ LeanSeq lean_locate(const DecParams& p, int B, int64_t target, int lane) {
   int64_t pre = 0;
   int nz = 0;
   for (int b0 = 0; b0 < B; b0 += 64) {
     const int b = b0 + lane;
-    const int n = b < B ? (min(max(p.lens[b], 0), p.capacity) + T - 1) / T : 0;
+    const int n = b < B ? (lean_rows<MQ>(p, p.lens[b]) + T - 1) / T : 0;
     const int incl = wave_incl_scan(n, lane);
     const int nzi = wave_incl_scan(n > 0 ? 1 : 0, lane);
     const uint64_t hit = __builtin_amdgcn_ballot_w64(b < B && (int64_t)p.Hkv * (pre + incl) > target);
@@ -515,7 +539,7 @@ __device__ __forceinline__ int64_t lean_unit_of(int64_t t, int64_t A, int64_t U)
   return ((t + 1) * U - 1) / A;
 }
 
-template <int D, class TL>
+template <int D, class TL, bool MQ>
 __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, int64_t U) {
   constexpr int T = TL::T, CPR = TL::CPR;
   static_assert(TL::NST == 2, "the lean decode keeps one tile in flight");
@@ -525,13 +549,14 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
   const uint32_t qlds = lds0 + 2 * TL::STAGE;
 
   const int lane = threadIdx.x;
-  const int col = lane & 15;
+  const int col = lane & 15;  // MFMA column: query qi = col / G, query head h G + col % G
   const int g4 = lane >> 4;
   const int G = p.group;
+  const int C = MQ ? p.Nq * G : G;  // columns in use (at most 16)
   const int Hkv = p.Hkv;
   const int64_t u = blockIdx.x;
 
-  const int64_t A = (int64_t)Hkv * lean_total<T>(p, B, lane);
+  const int64_t A = (int64_t)Hkv * lean_total<T, MQ>(p, B, lane);
   if (A == 0) return;
   // run [t0, t1) of this unit; A = q U + r keeps the products in range
   const int64_t qa = A / U, ra = A % U;
@@ -546,7 +571,7 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
   };
   Cur cc;
   {
-    const LeanSeq sq = lean_locate<T>(p, B, t0, lane);
+    const LeanSeq sq = lean_locate<T, MQ>(p, B, t0, lane);
     const int64_t r = t0 - (int64_t)Hkv * sq.pre;
     cc.b = sq.b;
     cc.nb = sq.nb;
@@ -563,14 +588,22 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
     c.nz += 1;
     do {
       ++c.b;
-      c.nb = c.b < B ? lean_tiles_uniform<T>(p, c.b) : 1;
+      c.nb = c.b < B ? lean_tiles_uniform<T, MQ>(p, c.b) : 1;
     } while (c.nb == 0);
   };
 
   const int kv_row = Hkv * D * 2;
   constexpr int QD = (QBYTES + 1023) / 1024;  // at most this many 16-byte loads per lane for the query rows
-  const int qbytes = G * D * 2;
+  const int qbytes = C * D * 2;
   const int qd = (qbytes + 1023) / 1024;
+  // byte offset of this lane's 16-byte piece j of a pair's query rows (column
+  // by column, D * 2 bytes each) from query 0, head h G of its sequence
+  auto q_off = [&](int j) {
+    const int x = min((j * 64 + lane) * 16, qbytes - 16);
+    if constexpr (!MQ) return (uint32_t)x;  // one query: the G rows are contiguous
+    const int cl = x / (D * 2), qq = cl / G;
+    return (uint32_t)(((qq * p.Hq + (cl - qq * G)) * D * 2) + (x - cl * D * 2));
+  };
   int dma_row[TL::DMA], dma_col[TL::DMA];
 #pragma unroll
   for (int j = 0; j < TL::DMA; ++j) {
@@ -579,18 +612,31 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
     dma_col[j] = ((slot % CPR) ^ swz<CPR>(slot / CPR)) * 16;
   }
   // tile k of the run (cursor c) into stage k % 2; a tile that starts a
-  // pair is preceded by the pair's query rows (G x D, contiguous in q) into
-  // query buffer `qb`
+  // pair is preceded by the pair's query rows (C x D) into query buffer
+  // `qb`, and a tile that appended rows fall in by their cache writes
   auto issue = [&](const Cur& c, int k, int qb) {
     if (c.i == 0 || k == 0) {
-      const char* qs = p.q + ((int64_t)c.b * p.Hq + (int64_t)c.h * G) * D * 2;
+      const char* qs = p.q + ((int64_t)c.b * p.Nq * p.Hq + (int64_t)c.h * G) * D * 2;
 #pragma unroll
       for (int j = 0; j < QD; ++j)
-        if (j < qd) dma16(qs, (uint32_t)min((j * 64 + lane) * 16, qbytes - 16), qlds + qb * QBYTES + j * 1024);
+        if (j < qd) dma16(qs, q_off(j), qlds + qb * QBYTES + j * 1024);
     }
-    const int len = c.i == c.nb - 1 ? min(max(((const __attribute__((address_space(4))) int32_t*)p.lens)[c.b], 0),
-                                          p.capacity)
-                                    : (c.i + 1) * T;
+    if (MQ && p.n_new > 0) {
+      const int base = min(max(lean_len_uniform(p, c.b), 0), p.capacity);
+      const int r0 = max(c.i * T, base), r1 = min((c.i + 1) * T, min(base + p.n_new, p.capacity));
+      if (r0 < r1) {
+        for (int idx = lane; idx < (r1 - r0) * CPR; idx += 64) {
+          const int r = r0 + idx / CPR, ch = idx % CPR;
+          const int64_t src = (((int64_t)c.b * p.Nq + (r - base)) * Hkv + c.h) * D * 2 + ch * 16;
+          const int64_t dst = (cache_row(p, c.b, r) * Hkv + c.h) * D * 2 + ch * 16;
+          *reinterpret_cast<u32x4*>(p.kc + dst) = *reinterpret_cast<const u32x4*>(p.kn + src);
+          *reinterpret_cast<u32x4*>(p.vc + dst) = *reinterpret_cast<const u32x4*>(p.vn + src);
+        }
+        // the rows are in memory before this wavefront's tile loads read them
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+    }
+    const int len = c.i == c.nb - 1 ? lean_rows<MQ>(p, lean_len_uniform(p, c.b)) : (c.i + 1) * T;
     const int last = len - 1 - c.i * T;  // rows past the end re-read the last key (masked later)
     const int64_t row = cache_row_uniform(p, c.b, c.i * T);
     const char* ks = p.kc + (row * Hkv + c.h) * D * 2;
@@ -622,7 +668,11 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
   bf16x8 qf[D / 32];
   f32x4 acc[D / 16];
   float m = -INFINITY, l = 0.f;
-  const bool cvalid = col < G;
+  const bool cvalid = col < C;
+  const int qi = MQ && cvalid ? col / G : (MQ ? p.Nq - 1 : 0);
+  // last key this lane's column sees in the pair being computed, and the
+  // smallest such key over the columns (tiles past it are masked)
+  int lastkey = 0, minkey = 0;
   int qbuf = 0;  // query buffer of the pair being computed
 
   Cur ic = cc;  // issue cursor, one tile ahead
@@ -650,7 +700,7 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
     }
     const bool seg_start = k == 0 || cc.i == 0;
     if (seg_start) {
-      // this pair's query rows: column col is query head h G + col
+      // this pair's query rows: column col is query qi, query head h G + col - qi G
 #pragma unroll
       for (int ks = 0; ks < D / 32; ++ks) {
         const bf16x8 x = *(const LDS3 bf16x8*)(uintptr_t)(qlds + qbuf * QBYTES + (col * D + ks * 32 + g4 * 8) * 2);
@@ -660,12 +710,23 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
       for (int dt = 0; dt < D / 16; ++dt) acc[dt] = f32x4{};
       m = -INFINITY;
       l = 0.f;
+      if constexpr (MQ) {
+        // query qi is bottom-right aligned with the held and appended rows:
+        // with causal masking it sees keys j <= held + appended - Nq + qi
+        const int held = lean_len_uniform(p, cc.b);
+        const int len = lean_rows<MQ>(p, held);
+        const int n_all = min(max(held, 0), p.capacity) + p.n_new;
+        lastkey = p.causal ? min(len - 1, n_all - p.Nq + qi) : len - 1;
+        minkey = p.causal ? min(len - 1, n_all - p.Nq) : len - 1;
+      }
     }
     const uint32_t stg = lds0 + (uint32_t)((k & 1) * TL::STAGE);
     const bool last_of_pair = cc.i == cc.nb - 1;
-    if (last_of_pair) {
-      const int len = min(max(((const __attribute__((address_space(4))) int32_t*)p.lens)[cc.b], 0), p.capacity);
+    if (!MQ && last_of_pair) {
+      const int len = lean_rows<MQ>(p, lean_len_uniform(p, cc.b));
       dec_tile<D, TL, true>(acc, m, l, qf, k_off, v_off, stg, len - 1 - cc.i * T - 4 * g4, p.c);
+    } else if (MQ && (last_of_pair || (cc.i + 1) * T - 1 > minkey)) {
+      dec_tile<D, TL, true>(acc, m, l, qf, k_off, v_off, stg, lastkey - cc.i * T - 4 * g4, p.c);
     } else {
       dec_tile<D, TL, false>(acc, m, l, qf, k_off, v_off, stg, 0, p.c);
     }
@@ -675,10 +736,10 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
       const int64_t slot = u + (int64_t)Hkv * cc.nz + cc.h;
       if (cvalid) {
         const float inv = lt > 0.f ? 1.f / lt : 0.f;
-        float* po = p.part_o + (slot * G + col) * D;
+        float* po = p.part_o + (slot * C + col) * D;
 #pragma unroll
         for (int dt = 0; dt < D / 16; ++dt) *reinterpret_cast<f32x4*>(po + dt * 16 + 4 * g4) = acc[dt] * inv;
-        if (g4 == 0) p.part_lse[slot * G + col] = lt > 0.f ? m + log2_fast(lt) : -INFINITY;
+        if (g4 == 0) p.part_lse[slot * C + col] = lt > 0.f ? m + log2_fast(lt) : -INFINITY;
       }
     }
     // the query buffer a new pair's rows went into
@@ -688,23 +749,26 @@ __global__ __launch_bounds__(64, 2) void decode_lean_kernel(DecParams p, int B, 
   }
 }
 
-// One wavefront per (sequence, query head): merge the parts of its pair in
-// unit order with weights 2^(L_s - max L).
-template <int D, int T>
+// One wavefront per (sequence, query, query head): merge the parts of its
+// pair's column in unit order with weights 2^(L_s - max L).
+template <int D, int T, bool MQ>
 __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, int B, int64_t U) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // b * Hq + hq
-  if (row >= B * p.Hq) return;
-  const int b = row / p.Hq, hq = row - b * p.Hq;
+  const int Nq = MQ ? p.Nq : 1;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b Nq + qi) Hq + hq: the row of o
+  if (row >= B * Nq * p.Hq) return;
+  const int b = row / (Nq * p.Hq), qh = row - b * Nq * p.Hq;
+  const int qi = MQ ? qh / p.Hq : 0, hq = qh - qi * p.Hq;
   const int G = p.group;
-  const int h = hq / G, g = hq - h * G;
-  const int64_t A = (int64_t)p.Hkv * lean_total<T>(p, B, lane);
+  const int C = Nq * G;
+  const int h = hq / G, g = qi * G + (hq - h * G);  // g: the column
+  const int64_t A = (int64_t)p.Hkv * lean_total<T, MQ>(p, B, lane);
   // P(b), n_b and NZ(b) from the same scan the units used
   int64_t pre = 0;
   int nz = 0, nb = 0;
   for (int b0 = 0; b0 <= b; b0 += 64) {
     const int bb = b0 + lane;
-    const int n = bb < B ? (min(max(p.lens[bb], 0), p.capacity) + T - 1) / T : 0;
+    const int n = bb < B ? (lean_rows<MQ>(p, p.lens[bb]) + T - 1) / T : 0;
     const int incl = wave_incl_scan(bb < b ? n : 0, lane);
     const int nzi = wave_incl_scan(bb < b && n > 0 ? 1 : 0, lane);
     if (b < b0 + 64) nb = __shfl(n, b - b0, 64);
@@ -719,7 +783,7 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
     const int64_t u0 = lean_unit_of(s0, A, U), u1 = lean_unit_of(s0 + nb - 1, A, U);
     const int64_t slot0 = u0 + (int64_t)p.Hkv * nz + h;
     const int n = (int)(u1 - u0 + 1);
-    const float* pl = p.part_lse + slot0 * G + g;
+    const float* pl = p.part_lse + slot0 * C + g;
     // with more units than tiles some units own no tile and write nothing:
     // their slots are skipped (unit u's run is empty iff its start equals
     // the next unit's)
@@ -735,8 +799,8 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
 #pragma unroll
       for (int uu = 0; uu < UG; ++uu) {
         const int s = min(s0p + uu, n - 1);
-        ls[uu] = pl[(int64_t)s * G];
-        const float* src = p.part_o + ((slot0 + s) * G + g) * D + lane * PER;
+        ls[uu] = pl[(int64_t)s * C];
+        const float* src = p.part_o + ((slot0 + s) * C + g) * D + lane * PER;
 #pragma unroll
         for (int e = 0; e < PER; ++e) po[uu][e] = src[e];
       }
@@ -768,7 +832,9 @@ __global__ __launch_bounds__(256) void decode_lean_combine_kernel(DecParams p, i
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
 #pragma unroll
   for (int e = 0; e < PER; ++e) reinterpret_cast<bf16*>(p.o)[(int64_t)row * D + lane * PER + e] = (bf16)(o[e] * inv);
-  if (lane == 0 && p.lse != nullptr) p.lse[row] = wsum > 0.f ? (M + log2_fast(wsum)) * kLn2 : -INFINITY;
+  if (lane == 0 && p.lse != nullptr)
+    p.lse[MQ ? ((int64_t)b * p.Hq + hq) * Nq + qi : (int64_t)row] = wsum > 0.f ? (M + log2_fast(wsum)) * kLn2
+                                                                           : -INFINITY;
 }
 
 template <int D, class TL>
@@ -812,8 +878,8 @@ hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// The balanced decode: one query per sequence, nothing appended, at least
-// two parts per pair on average (num_splits - 1 units per pair).
+// The balanced decode: at most 16 (query, query head) columns per pair, at
+// least two parts per pair on average (num_splits - 1 units per pair).
 template <int D, class TL>
 hipError_t launch_lean(const DecodeArgs& a, hipStream_t stream, int64_t U) {
   DecParams p;
@@ -834,19 +900,28 @@ hipError_t launch_lean(const DecodeArgs& a, hipStream_t stream, int64_t U) {
   p.page_size = a.page_size;
   p.pages_per_seq = a.pages_per_seq;
   p.num_pages = a.num_pages;
-  p.Nq = 1;
+  p.Nq = a.Nq;
   p.ncg = 1;
-  p.causal = 0;
-  p.n_new = 0;
-  p.kn = nullptr;
-  p.vn = nullptr;
+  p.causal = a.causal;
+  p.n_new = a.k_new != nullptr ? a.Nq : 0;
+  p.kn = static_cast<const char*>(a.k_new);
+  p.vn = static_cast<const char*>(a.v_new);
   p.part_o = static_cast<float*>(a.workspace);
-  p.part_lse = p.part_o + (size_t)a.B * a.Hq * p.S * D;
-  hipLaunchKernelGGL((decode_lean_kernel<D, TL>), dim3((unsigned)U), dim3(64), 0, stream, p, a.B, U);
+  p.part_lse = p.part_o + (size_t)a.B * a.Nq * a.Hq * p.S * D;
+  const bool mq = a.Nq > 1 || a.k_new != nullptr;
+  if (mq)
+    hipLaunchKernelGGL((decode_lean_kernel<D, TL, true>), dim3((unsigned)U), dim3(64), 0, stream, p, a.B, U);
+  else
+    hipLaunchKernelGGL((decode_lean_kernel<D, TL, false>), dim3((unsigned)U), dim3(64), 0, stream, p, a.B, U);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = a.B * a.Hq;
-  hipLaunchKernelGGL((decode_lean_combine_kernel<D, TL::T>), dim3((rows + 3) / 4), dim3(256), 0, stream, p, a.B, U);
+  const int rows = a.B * a.Nq * a.Hq;
+  if (mq)
+    hipLaunchKernelGGL((decode_lean_combine_kernel<D, TL::T, true>), dim3((rows + 3) / 4), dim3(256), 0, stream, p,
+                       a.B, U);
+  else
+    hipLaunchKernelGGL((decode_lean_combine_kernel<D, TL::T, false>), dim3((rows + 3) / 4), dim3(256), 0, stream, p,
+                       a.B, U);
   return hipGetLastError();
 }
 
@@ -863,11 +938,11 @@ using LeanTileSmall = DecTile<D, 32, 2>;
 constexpr int64_t kLeanSmallTilePairs = 256;
 bool lean_small_tiles(int d, int64_t pairs) { return (d == 64 || d == 128) && pairs >= kLeanSmallTilePairs; }
 
-// Units of the balanced decode, or 0 where it does not apply (several
-// queries, appended rows, no split, or sizes whose unit arithmetic would
+// Units of the balanced decode, or 0 where it does not apply (no split, a
+// shape decode_balanced turns away, or sizes whose unit arithmetic would
 // leave 64-bit range).
 int64_t lean_units(const DecodeArgs& a) {
-  if (a.Nq != 1 || a.k_new != nullptr || a.num_splits < 2 || a.B <= 0) return 0;
+  if (a.num_splits < 2 || !decode_balanced(a.B, a.Nq, a.Hq, a.Hkv, a.k_new != nullptr)) return 0;
   const int T = 32;  // the smallest tile any shape takes: the most tiles
   const int64_t U = (int64_t)(a.num_splits - 1) * a.B * a.Hkv;
   const double tiles = (double)a.B * a.Hkv * (((double)a.capacity + T - 1) / T);
@@ -886,6 +961,17 @@ int dec_variant() {
 
 }  // namespace
 
+// Whether a split decode call takes the balanced schedule: one query per
+// sequence with nothing appended always; several queries or appended rows
+// when their columns fit one MFMA group (Nq G <= 16) and there are at least
+// 64 (sequence, key/value head) pairs. Below that the position splits were
+// faster on MI355X (32 pairs, GQA 32/8, d = 128: 22.5 against 26.0 us),
+// from 64 pairs on the balanced schedule (64 pairs: 64.2 against 70.3 us).
+bool decode_balanced(int B, int Nq, int Hq, int Hkv, bool append) {
+  if (B <= 0 || Hkv <= 0 || (int64_t)Nq * (Hq / Hkv) > 16) return false;
+  return (Nq == 1 && !append) || (int64_t)B * Hkv >= 64;
+}
+
 int decode_chunk(int capacity, int num_splits) {
   const int per = (capacity + num_splits - 1) / num_splits;
   const int c = ((per + kSplitAlign - 1) / kSplitAlign) * kSplitAlign;
@@ -897,21 +983,23 @@ size_t decode_workspace_bytes(int B, int Hq, int d, int num_splits) {
   return (size_t)B * Hq * num_splits * ((size_t)d + 1) * sizeof(float);
 }
 
+// Resident workgroups per CU of the balanced decode (its one-query form;
+// the LDS ring and query buffers bound both forms alike).
 int decode_resident_per_cu(int d, int64_t pairs) {
   int n = 0;
   hipError_t e = hipErrorInvalidValue;
   switch (d) {
     case 64:
       e = lean_small_tiles(d, pairs)
-              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTileSmall<64>>, 64, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTile<64>>, 64, 0);
+              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTileSmall<64>, false>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<64, LeanTile<64>, false>, 64, 0);
       break;
     case 128:
       e = lean_small_tiles(d, pairs)
-              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTileSmall<128>>, 64, 0)
-              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTile<128>>, 64, 0);
+              ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTileSmall<128>, false>, 64, 0)
+              : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<128, LeanTile<128>, false>, 64, 0);
       break;
-    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<256, LeanTile<256>>, 64, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_lean_kernel<256, LeanTile<256>, false>, 64, 0); break;
     default: break;
   }
   if (e != hipSuccess) (void)hipGetLastError();  // leave no sticky error behind

@@ -173,11 +173,14 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu);
 
 /* A num_splits for the decode calls with appended rows or several queries
- * per sequence (fa_fwd_kvcache_append, fa_fwd_kvcache_paged_append), whose
- * split s covers keys [s c, (s+1) c) of every sequence: splits of about 1024
- * keys, at least enough to fill every resident workgroup (wgs_per_cu, or 0:
- * from the occupancy API for that kernel), at most 64 workgroups per
- * resident slot. Always >= 1 (1 also for invalid sizes). */
+ * per sequence (fa_fwd_kvcache_append, fa_fwd_kvcache_paged_append). With
+ * Nq * (Hq / Hkv) <= 16 those calls take the balanced decode and this is
+ * fa_kvcache_default_splits(B, Hkv, capacity, d, num_cus, wgs_per_cu).
+ * Wider calls split every sequence's keys by position, split s covering
+ * keys [s c, (s+1) c): splits of about 1024 keys, at least enough to fill
+ * every resident workgroup (wgs_per_cu, or 0: from the occupancy API for
+ * that kernel), at most 64 workgroups per resident slot. Always >= 1 (1
+ * also for invalid sizes). */
 int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacity, int d, int num_cus,
                                      int wgs_per_cu);
 
@@ -255,6 +258,10 @@ fa_status_t fa_fwd_kvcache_paged(const void* q, const void* kpages, const void* 
  * one stream. With Nq = 1 and nothing appended the results are bitwise
  * those of fa_fwd_kvcache. Nq * (Hq / Hkv) (query, head) pairs per key/value
  * head are served 16 per workgroup; each such group streams the cache once.
+ * With at most 16 of them and num_splits = S >= 2 the cache work is cut
+ * into (S - 1) B Hkv equal runs as in fa_fwd_kvcache, and a tile's appended
+ * rows are written by the workgroup that then reads that tile; with more,
+ * each sequence's keys are cut into S ranges by position.
  * FA_ERR_INVALID_ARG for Nq < 1 or only one of k_new / v_new. */
 fa_status_t fa_fwd_kvcache_append(const void* q, const void* k_new, const void* v_new, void* kcache, void* vcache,
                                   const int32_t* cache_seqlens, void* o, float* lse, int causal, int num_splits,

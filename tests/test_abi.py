@@ -126,12 +126,22 @@ def test_default_splits():
 
 
 def test_append_default_splits():
-    assert fa.fa_kvcache_append_default_splits(64, 1, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
-    assert fa.fa_kvcache_append_default_splits(1, 1, 8, 32, 8192, 128, 256, 3) == 96    # fill 768 slots
-    assert fa.fa_kvcache_append_default_splits(1, 1, 1, 1, 64, 128, 256, 3) == 1        # one block: cannot split
-    assert fa.fa_kvcache_append_default_splits(4096, 1, 8, 32, 8192, 128, 256, 3) == 1  # capped by the slot budget
+    # at most 16 (query, query head) columns per key/value head and at least
+    # 64 (sequence, key/value head) pairs: the balanced decode, whose rule is
+    # fa_kvcache_default_splits
+    for B, Nq, Hkv, Hq, cap, d in [(64, 1, 8, 32, 8192, 128), (64, 4, 8, 32, 8192, 128), (8, 1, 8, 32, 8192, 64),
+                                   (4096, 2, 8, 32, 8192, 128), (32, 2, 2, 16, 4096, 256), (64, 16, 1, 1, 64, 128)]:
+        assert (fa.fa_kvcache_append_default_splits(B, Nq, Hkv, Hq, cap, d, 256, 3)
+                == fa.fa_kvcache_default_splits(B, Hkv, cap, d, 256, 3)), (B, Nq, Hkv, Hq, cap, d)
+    assert fa.fa_kvcache_append_default_splits(64, 4, 8, 32, 8192, 128, 256, 3) == 3    # 512 pairs, 768 slots
     assert fa.fa_kvcache_append_default_splits(0, 1, 8, 32, 8192, 128, 256, 3) == 1
-    assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 8    # 2 column groups per head
+    # more columns, or fewer pairs: splits of the keys by position
+    assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
+    assert fa.fa_kvcache_append_default_splits(1, 8, 8, 32, 8192, 128, 256, 3) == 48    # fill 768 slots, 2 groups
+    assert fa.fa_kvcache_append_default_splits(1, 1, 8, 32, 8192, 128, 256, 3) == 96    # 8 pairs: fill 768 slots
+    assert fa.fa_kvcache_append_default_splits(1, 1, 1, 1, 64, 128, 256, 3) == 1        # one block: cannot split
+    assert fa.fa_kvcache_append_default_splits(1, 5, 1, 4, 64, 128, 256, 3) == 1
+    assert fa.fa_kvcache_append_default_splits(4096, 8, 8, 32, 8192, 128, 256, 3) == 1  # capped by the slot budget
 
 
 def test_paged_decode_host_validation():
