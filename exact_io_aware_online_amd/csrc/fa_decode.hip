@@ -16,8 +16,9 @@
 // Scores are S^T = K Q^T on the 16x16x32 bf16 MFMA with the G query heads
 // as columns (the other 16 - G columns are zero); P^T then feeds
 // O^T += V^T P^T from registers, the V^T operand read from the row-major V
-// tile with ds_read_b64_tr_b16. With one query per sequence and nothing
-// appended, the balanced form further down replaces the fixed splits.
+// tile with ds_read_b64_tr_b16. The balanced form further down replaces
+// the fixed splits for one query per sequence, and for several queries or
+// appended rows where decode_balanced says so.
 //
 // Partial results: O_s (normalised, fp32) and L_s = log2 of the split's sum
 // of 2^(t) in base-2 units; an empty split is never written, the combine
