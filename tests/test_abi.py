@@ -115,9 +115,11 @@ def test_default_splits():
     # single-query decode: about one balanced run per resident workgroup,
     # runs of at least ~8 tiles, no split with plenty of pairs
     assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 2      # 512 pairs, 512 slots
-    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 3      # 384 pairs: 768 runs
+    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 2      # 384 pairs: 384 runs, not 768
     assert fa.fa_kvcache_default_splits(128, 8, 8192, 128, 256, 2) == 2     # 1024 pairs, one run each
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 3      # 768 slots: 2 runs per pair
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 4) == 3      # 1024 slots: 2 runs per pair
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 2      # 768 slots: 1 whole run per pair
+    assert fa.fa_kvcache_default_splits(6, 8, 8192, 128, 256, 2) == 11     # 48 pairs: 480 runs on 512 slots
     assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 17      # capped by run length: 128 / 8 + 1
     assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one tile: nothing to balance
     assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # 4+ pairs per slot
@@ -133,7 +135,7 @@ def test_append_default_splits():
                                    (4096, 2, 8, 32, 8192, 128), (32, 2, 2, 16, 4096, 256), (64, 16, 1, 1, 64, 128)]:
         assert (fa.fa_kvcache_append_default_splits(B, Nq, Hkv, Hq, cap, d, 256, 3)
                 == fa.fa_kvcache_default_splits(B, Hkv, cap, d, 256, 3)), (B, Nq, Hkv, Hq, cap, d)
-    assert fa.fa_kvcache_append_default_splits(64, 4, 8, 32, 8192, 128, 256, 3) == 3    # 512 pairs, 768 slots
+    assert fa.fa_kvcache_append_default_splits(64, 4, 8, 32, 8192, 128, 256, 4) == 3    # 512 pairs, 1024 slots
     assert fa.fa_kvcache_append_default_splits(0, 1, 8, 32, 8192, 128, 256, 3) == 1
     # more columns, or fewer pairs: splits of the keys by position
     assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
