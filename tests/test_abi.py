@@ -120,6 +120,11 @@ def test_default_splits():
     assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 4) == 3      # 1024 slots: 2 runs per pair
     assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 2      # 768 slots: 1 whole run per pair
     assert fa.fa_kvcache_default_splits(6, 8, 8192, 128, 256, 2) == 11     # 48 pairs: 480 runs on 512 slots
+    # more pairs than slots: the fewest runs per pair whose waves leave <= 1/8 of the slot-time idle
+    assert fa.fa_kvcache_default_splits(136, 8, 8192, 128, 256, 4) == 6     # 1088 pairs: 5440 runs, 6 waves
+    assert fa.fa_kvcache_default_splits(160, 8, 8192, 128, 256, 4) == 4     # 1280 pairs: 3840 runs, 4 waves
+    assert fa.fa_kvcache_default_splits(240, 8, 4096, 128, 256, 4) == 2     # 1920 pairs: 2 waves, 1/16 idle
+    assert fa.fa_kvcache_default_splits(136, 8, 2048, 128, 256, 4) == 5     # runs of 8 tiles at most 4 a pair
     assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 17      # capped by run length: 128 / 8 + 1
     assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one tile: nothing to balance
     assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # 4+ pairs per slot
