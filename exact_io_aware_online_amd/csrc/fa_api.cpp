@@ -221,45 +221,38 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, 
   num_cus = clamp_count(num_cus, 1 << 16);
   wgs_per_cu = clamp_count(wgs_per_cu, 1 << 10);
   // The balanced decode runs (num_splits - 1) B Hkv equal runs of cache
-  // tiles: the most whole runs per pair that still give every run a
-  // resident workgroup at once, each run at least about 8 tiles of 64 keys
-  // long so its start is amortised. (Rounding the runs per pair up instead
-  // left a few runs to start after the first wave had finished: 10-30%
-  // slower on MI355X wherever the pairs do not divide the slots, e.g. 48
-  // pairs on 512 slots 38.1 against 30.6 us.) With
-  // four or more pairs per resident slot, or a cache of one tile, one pass
-  // per pair without a combine is as balanced. (Two runs per workgroup
-  // measured 0-1.8% faster where full caches make long runs, but up to 11%
-  // slower where the sequences are much shorter than the capacity, which
-  // is all this function knows of them.)
+  // tiles, each ideally on a resident workgroup of its own. Runs come in
+  // waves of `slots`; a wave that holds few runs streams at a fraction of
+  // the bandwidth. So take the fewest runs per pair whose waves leave at
+  // most 1/8 of the slot-time idle (else the least idle), among 1 .. max(8,
+  // slots / pairs) runs per pair, each run at least about 8 tiles of 64
+  // keys long so its start is amortised. Measured on MI355X (GQA 32/8, d =
+  // 128, lengths uniform over the upper seven eighths of the capacity): 48
+  // pairs on 512 slots 30.6 us with 480 runs against 38.1 us with 528 (a
+  // second wave of 16), 1088 pairs on 1024 slots 406 us with 5 runs per
+  // pair against 482 us with one, 600 pairs 235 us with 3 runs per pair
+  // against 257 us with one. With four or more pairs per resident slot, or
+  // a cache of one tile, one pass per pair without a combine is as
+  // balanced.
   const long slots = (long)num_cus * wgs_per_cu;
   const long pairs = (long)B * Hkv;
   const long tiles = ((long)capacity + 63) / 64;
   if (pairs >= 4 * slots || tiles <= 1) return 1;
   const long by_len = tiles / 8 > 1 ? tiles / 8 : 1;
-  long per_pair = slots / pairs > 1 ? slots / pairs : 1;
-  if (pairs > slots) {
-    // More pairs than slots: the runs come in waves, and a last wave that
-    // holds only a few runs streams at a fraction of the bandwidth. Take the
-    // fewest runs per pair (up to 8) whose waves leave at most 1/8 of the
-    // slot-time idle, else the least idle (1088 pairs on 1024 slots: 1 run
-    // each 499.7 us, 4 runs each 420.0 us; 1280 pairs: 572.0 against 507.5
-    // us with 3 runs each; measured on MI355X, lengths uniform over the
-    // upper seven eighths of the capacity).
-    long best = 1, best_idle = 0, best_waves = 1;
-    for (long k = 1; k <= 8 && k <= by_len; ++k) {
-      const long u = k * pairs, waves = (u + slots - 1) / slots;
-      const long idle = waves * slots - u;  // slot-runs left idle by the last wave
-      if (k == 1 || idle * best_waves < best_idle * waves) {
-        best = k;
-        best_idle = idle;
-        best_waves = waves;
-      }
-      if (8 * idle <= waves * slots) break;
+  long kmax = slots / pairs > 8 ? slots / pairs : 8;
+  if (kmax > by_len) kmax = by_len;
+  if (kmax > 65534) kmax = 65534;
+  long per_pair = 1, best_idle = 0, best_waves = 1;
+  for (long k = 1; k <= kmax; ++k) {
+    const long u = k * pairs, waves = (u + slots - 1) / slots;
+    const long idle = waves * slots - u;  // slot-runs left idle by the last wave
+    if (k == 1 || idle * best_waves < best_idle * waves) {
+      per_pair = k;
+      best_idle = idle;
+      best_waves = waves;
     }
-    per_pair = best;
+    if (8 * idle <= waves * slots) break;
   }
-  if (per_pair > by_len) per_pair = by_len;
   long s = 1 + per_pair;
   if (s > 65535) s = 65535;
   return (int)s;

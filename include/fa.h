@@ -166,11 +166,11 @@ size_t fa_fwd_kvcache_workspace_size(int B, int Hq, int d, int num_splits);
  * selects (2 if no device can be queried); counts above 65536 CUs and 1024
  * workgroups per CU are taken as those. With num_splits = S >= 2 the
  * single-query decode cuts the cache work of all sequences into
- * (S - 1) B Hkv equal runs; the default takes the most whole runs per pair
- * (at least one) that the resident workgroups hold at once, or, with more
- * pairs than resident workgroups, the fewest runs per pair (up to 8) whose
- * waves leave at most 1/8 of the workgroup time idle (else the least idle);
- * each run at least ~8 tiles of 64 keys, and 1 (no split) when
+ * (S - 1) B Hkv equal runs, which the resident workgroups take in waves;
+ * the default takes the fewest runs per pair (1 .. max(8, resident
+ * workgroups / pairs)) whose waves leave at most 1/8 of the workgroup time
+ * idle (else the least idle), each run at least ~8 tiles of 64 keys, and 1
+ * (no split) when
  * there are four or more (sequence, key/value head) pairs per resident
  * workgroup. Always >= 1. */
 int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, int wgs_per_cu);

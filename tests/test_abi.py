@@ -112,24 +112,26 @@ def test_workspace_size_formula():
 
 
 def test_default_splits():
-    # single-query decode: about one balanced run per resident workgroup,
-    # runs of at least ~8 tiles, no split with plenty of pairs
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 2      # 512 pairs, 512 slots
-    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 2      # 384 pairs: 384 runs, not 768
-    assert fa.fa_kvcache_default_splits(128, 8, 8192, 128, 256, 2) == 2     # 1024 pairs, one run each
+    # single-query decode: the fewest runs per pair whose waves of resident
+    # workgroups leave at most 1/8 of the slot-time idle (else the least
+    # idle), runs of at least ~8 tiles, no split with plenty of pairs
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 2) == 2      # 512 pairs, 512 slots: one wave
     assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 4) == 3      # 1024 slots: 2 runs per pair
-    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 2      # 768 slots: 1 whole run per pair
-    assert fa.fa_kvcache_default_splits(6, 8, 8192, 128, 256, 2) == 11     # 48 pairs: 480 runs on 512 slots
-    # more pairs than slots: the fewest runs per pair whose waves leave <= 1/8 of the slot-time idle
+    assert fa.fa_kvcache_default_splits(64, 8, 8192, 128, 256, 3) == 4      # 768 slots: 1536 runs, 2 full waves
+    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 2) == 5      # 384 pairs: 1536 runs, 3 full waves
+    assert fa.fa_kvcache_default_splits(48, 8, 8192, 128, 256, 4) == 6      # 1920 runs on 1024 slots, 1/16 idle
+    assert fa.fa_kvcache_default_splits(75, 8, 8192, 128, 256, 4) == 4      # 600 pairs: 1800 runs, 2 waves
+    assert fa.fa_kvcache_default_splits(6, 8, 8192, 128, 256, 2) == 11      # 48 pairs: 480 runs, not 528
+    assert fa.fa_kvcache_default_splits(128, 8, 8192, 128, 256, 2) == 2     # 1024 pairs, 2 full waves
     assert fa.fa_kvcache_default_splits(136, 8, 8192, 128, 256, 4) == 6     # 1088 pairs: 5440 runs, 6 waves
     assert fa.fa_kvcache_default_splits(160, 8, 8192, 128, 256, 4) == 4     # 1280 pairs: 3840 runs, 4 waves
     assert fa.fa_kvcache_default_splits(240, 8, 4096, 128, 256, 4) == 2     # 1920 pairs: 2 waves, 1/16 idle
-    assert fa.fa_kvcache_default_splits(136, 8, 2048, 128, 256, 4) == 5     # runs of 8 tiles at most 4 a pair
+    assert fa.fa_kvcache_default_splits(136, 8, 2048, 128, 256, 4) == 5     # runs of 8 tiles: at most 4 a pair
     assert fa.fa_kvcache_default_splits(1, 8, 8192, 128, 256, 3) == 17      # capped by run length: 128 / 8 + 1
+    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 128, 256, 3) == 337  # 672 of 768 slots: 1/8 idle
     assert fa.fa_kvcache_default_splits(1, 1, 64, 128, 256, 3) == 1         # one tile: nothing to balance
     assert fa.fa_kvcache_default_splits(4096, 8, 8192, 128, 256, 3) == 1    # 4+ pairs per slot
     assert fa.fa_kvcache_default_splits(0, 8, 8192, 128, 256, 3) == 1
-    assert fa.fa_kvcache_default_splits(2, 1, 1000000, 128, 256, 3) == 385
 
 
 def test_append_default_splits():
