@@ -167,3 +167,63 @@ def test_graph_replays_of_backward_and_fp8_equal_eager_calls():
         note(f"  replay {rep}: dq, dk, dv, the FP8 codes and scales, O and LSE equal to the eager calls")
     del g
     torch.cuda.synchronize()
+
+
+def test_graph_replays_of_balanced_append_equal_eager_calls():
+    m = fa()
+    dev = torch.device("cuda")
+    note("graph capture: fa_fwd_kvcache_append, 2 new tokens, 64 (sequence, KV head) pairs (balanced schedule)")
+    B, Nq, Hq, Hkv, cap, d = 32, 2, 8, 2, 1024, 128
+    sc = float(np.float32(1.0 / math.sqrt(d)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(95)
+    rnd = lambda *s: torch.randn(s, generator=gen, device=dev).to(torch.bfloat16)
+    q, kn, vn = rnd(B, Nq, Hq, d), rnd(B, Nq, Hkv, d), rnd(B, Nq, Hkv, d)
+    kc, vc = rnd(B, cap, Hkv, d), rnd(B, cap, Hkv, d)
+    lens = torch.randint(0, cap - Nq + 1, (B,), generator=gen, device=dev, dtype=torch.int32)
+    S = m.fa_kvcache_append_default_splits(B, Nq, Hkv, Hq, cap, d)
+    assert S >= 2
+    ws = torch.empty(m.fa_fwd_kvcache_workspace_size(B * Nq, Hq, d, S), dtype=torch.uint8, device=dev)
+
+    def outputs():
+        return torch.empty_like(q), torch.empty(B, Hq, Nq, dtype=torch.float32, device=dev)
+
+    def run(o, lse):
+        m.fa_fwd_kvcache_append(q, kc, vc, lens, kn, vn, causal=True, o=o, lse=lse, num_splits=S, scale=sc,
+                                workspace=ws)
+
+    graph_out = outputs()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(*graph_out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run(*graph_out)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (q, kn, vn, kc, vc):
+            t.copy_(torch.randn(t.shape, generator=gen, device=dev).to(t.dtype))
+        lens.copy_(torch.randint(0, cap - Nq + 1, (B,), generator=gen, device=dev, dtype=torch.int32))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = [t.clone() for t in graph_out]
+        cache_after = (kc.clone(), vc.clone())
+        eager = outputs()
+        run(*eager)
+        torch.cuda.synchronize()
+        for name, a, b in zip(("O", "LSE"), got, eager):
+            assert torch.equal(a.view(torch.int8), b.view(torch.int8)), (rep, name)
+        # the appended rows are in the cache, and the result is the attention of the grown cache
+        b0 = int(lens[0])
+        assert torch.equal(cache_after[0][0, b0:b0 + Nq], kn[0]) and torch.equal(cache_after[1][0, b0:b0 + Nq], vn[0])
+        k2, v2, o_ref, l_ref = O.decode_append(f64(q[:1]), f64(kc[:1]), f64(vc[:1]), [b0], f64(kn[:1]), f64(vn[:1]),
+                                               True, sc)
+        assert np.max(np.abs(f64(got[0][:1]) - o_ref)) <= 2e-2
+        assert np.max(np.abs(f64(got[1][:1]) - l_ref)) <= 1e-3
+        note(f"  replay {rep}: equal to the eager call; sequence 0 within the oracle bars")
+    del g
+    torch.cuda.synchronize()
