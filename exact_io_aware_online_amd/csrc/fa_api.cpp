@@ -273,10 +273,12 @@ int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacit
   // workgroups; a workgroup serves 16 (query, query head) columns.
   const long groups = ((long)Nq * (Hq / Hkv) + 15) / 16;
   const long by_len = ((long)capacity + 1023) / 1024;
-  // beyond ~64 workgroups per resident slot the extra splits only add combine
-  // work; with that many (sequence, KV head, column group) items already,
-  // one split (the test avoids forming the possibly huge product)
-  const long max_wgs = 64L * num_cus * wgs_per_cu;
+  // beyond about four waves of split workgroups the extra splits only add
+  // partials and combine work (32 columns, B = 64, GQA 32/8, d = 128: 466 us
+  // at 2 splits against 498 us at 8; 5 queries: 456 against 474 us); with
+  // that many (sequence, KV head, column group) items already, one split
+  // (the test avoids forming the possibly huge product)
+  const long max_wgs = 4L * num_cus * wgs_per_cu;
   if (groups >= max_wgs || (long)B * Hkv > (max_wgs - 1) / groups) return 1;
   const long items = (long)B * Hkv * groups;
   const long by_fill = ((long)num_cus * wgs_per_cu + items - 1) / items;

@@ -182,7 +182,7 @@ int fa_kvcache_default_splits(int B, int Hkv, int capacity, int d, int num_cus, 
  * Wider calls split every sequence's keys by position, split s covering
  * keys [s c, (s+1) c): splits of about 1024 keys, at least enough to fill
  * every resident workgroup (wgs_per_cu, or 0: from the occupancy API for
- * that kernel), at most 64 workgroups per resident slot. Always >= 1 (1
+ * that kernel), at most 4 workgroups per resident slot. Always >= 1 (1
  * also for invalid sizes). */
 int fa_kvcache_append_default_splits(int B, int Nq, int Hkv, int Hq, int capacity, int d, int num_cus,
                                      int wgs_per_cu);

@@ -145,7 +145,8 @@ def test_append_default_splits():
     assert fa.fa_kvcache_append_default_splits(64, 4, 8, 32, 8192, 128, 256, 4) == 3    # 512 pairs, 1024 slots
     assert fa.fa_kvcache_append_default_splits(0, 1, 8, 32, 8192, 128, 256, 3) == 1
     # more columns, or fewer pairs: splits of the keys by position
-    assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
+    assert fa.fa_kvcache_append_default_splits(64, 8, 8, 32, 8192, 128, 256, 3) == 3    # 1024 items: 4 waves at most
+    assert fa.fa_kvcache_append_default_splits(16, 8, 8, 32, 8192, 128, 256, 3) == 8    # ~1024-key splits
     assert fa.fa_kvcache_append_default_splits(1, 8, 8, 32, 8192, 128, 256, 3) == 48    # fill 768 slots, 2 groups
     assert fa.fa_kvcache_append_default_splits(1, 1, 8, 32, 8192, 128, 256, 3) == 96    # 8 pairs: fill 768 slots
     assert fa.fa_kvcache_append_default_splits(1, 1, 1, 1, 64, 128, 256, 3) == 1        # one block: cannot split
